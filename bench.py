@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""GDN prefill benchmark: 36 layers of pre -> scan -> post at T=2048.
+
+One step = one pass of the whole path (gdn_pre, gdn_scan, gdn_post for each
+of the 36 layers, launched in order on one stream) over one 2048-token batch
+at production width (16 key heads, 48 value heads, head dim 128, fp16
+activations and weights, fp32 state).  Every layer has its own inputs, state,
+history and output buffers, all resident in HBM before timing starts; the
+fp32 intermediates live in one workspace reused layer after layer, as in a
+real prefill.
+
+Prints ONE JSON line: tokens/s for the fp16-output run (the headline), the
+fp32-output run beside it, per-stage times from HIP events recorded on the
+launch stream inside the timed region, the scan's roofline fraction, and
+the fp64 oracle timed on the host cores on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/sec (pre+scan+post, 36 layers, T=2048); % of roofline"
+# MI355X published peaks
+HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3      # published, counts packed-FP32 FMAs
+FP32_VECTOR_UNPACKED_TFLOPS = 78.6   # 256 CU x 64 lanes x 2 flop x 2.4 GHz (no packed FP32)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_counters.json")
+
+
+def scan_flops(T, hv, dv=128, dk=128):
+    # S k: 2, decay + rank-1 write: 3, S q: 2 flop per state element per token
+    return 7.0 * T * hv * dv * dk
+
+
+def pre_bytes(T, hk, hv, io_bytes=2, n_seq=1):
+    C = 2 * hk * 128 + hv * 128
+    per_tok = C * io_bytes + 2 * hv * io_bytes + (2 * hk * 128 + hv * 128) * 4 + 2 * hv * 4
+    fixed = C * 4 * io_bytes + 2 * hv * io_bytes + n_seq * 2 * 3 * C * io_bytes
+    return T * per_tok + fixed
+
+
+def scan_bytes(T, hk, hv, n_seq=1):
+    per_tok = (2 * hk * 128 + hv * 128) * 4 + 2 * hv * 4 + hv * 128 * 4
+    return T * per_tok + n_seq * 2 * hv * 128 * 128 * 4
+
+
+def post_bytes(T, hv, io_bytes=2, out_bytes=2):
+    return T * hv * 128 * (4 + io_bytes + out_bytes) + 128 * io_bytes
+
+
+def kernel_source_hash(name):
+    p = os.path.join(ROOT, "gated_deltanet_linear_pre_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per scan launch from rocprofv3 counters, if they were taken on
+    the scan kernel as it is now (source hash match); else None."""
+    try:
+        d = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash("gdn_scan.hip"):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle, as it stands, on a prefix of layer 0's tokens (all 48
+    heads, all three stages), doubling the prefix until a run takes ~1/3 of
+    the budget; reports tokens/s of the last run."""
+    import numpy as np
+    from gated_deltanet_linear_pre_amd import synth
+    from oracle import gdn_oracle as orc
+
+    w = synth.WORKLOADS["prod36_t2048_fp16out"]
+    inp = synth.layer_inputs(w, 0)
+    dims = orc.Dims(w.hk, w.hv)
+    n, spent, rate = 8, 0.0, None
+    while True:
+        part = dict(inp)
+        for k in ("qkv", "a", "b", "z"):
+            part[k] = inp[k][:n]
+        t0 = time.perf_counter()
+        orc.layer(dims, np.array([0, n]), part)
+        dt = time.perf_counter() - t0
+        spent += dt
+        rate = n / dt
+        if dt > budget_s / 3 or n >= w.total_T or spent > budget_s:
+            break
+        n = min(2 * n, w.total_T)
+    return dict(value=rate, unit="tokens/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"layer 0 of the 36-layer T=2048 workload, first {n} tokens, all 48 value "
+                       f"heads, pre+scan+post in fp64 ({dt:.1f} s for that run)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by value heads with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from gated_deltanet_linear_pre_amd import binding as B
+    from gated_deltanet_linear_pre_amd import synth
+    from gated_deltanet_linear_pre_amd.buffers import TORCH_DTYPE, upload
+
+    def log(*a):
+        if not args.quiet:
+            print("[bench]", *a, file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w16 = synth.WORKLOADS["prod36_t2048_fp16out"]
+    L = args.layers
+    T, hk, hv = w16.total_T, w16.hk, w16.hv
+
+    # ---- inputs for all layers, resident in HBM --------------------------
+    t0 = time.perf_counter()
+    layers = []
+    for l in range(L):
+        inp = synth.layer_inputs(w16, l)
+        layers.append({k: upload(v, dev) for k, v in inp.items()})
+        if l % 6 == 5:
+            log(f"generated layer {l + 1}/{L} ({time.perf_counter() - t0:.1f}s)")
+    cu = upload(w16.cu_seqlens(), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    qn = torch.empty((T, hk, 128), **f32)
+    kn = torch.empty((T, hk, 128), **f32)
+    vc = torch.empty((T, hv, 128), **f32)
+    g = torch.empty((T, hv), **f32)
+    beta = torch.empty((T, hv), **f32)
+    o = torch.empty((T, hv, 128), **f32)
+    stream = torch.cuda.current_stream()
+
+    def run(out, steps, warmup):
+        ys = [torch.empty((T, hv * 128), dtype=TORCH_DTYPE[out], device=dev) for _ in range(L)]
+        shape = B.make_shape(hk, hv, 1, T, T, io="f16", out=out)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L * steps)]
+
+        def step(events=None):
+            for l, d in enumerate(layers):
+                e = events[l] if events else None
+                if e: e[0].record(stream)
+                B.gdn_pre(shape, cu, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"],
+                          d["dt_bias"], d["hist"], qn, kn, vc, g, beta, stream=stream)
+                if e: e[1].record(stream)
+                B.gdn_scan(shape, cu, qn, kn, vc, g, beta, d["S0"], o, stream=stream)
+                if e: e[2].record(stream)
+                B.gdn_post(shape, o, d["z"], d["gamma"], ys[l], stream=stream)
+                if e: e[3].record(stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for s in range(steps):
+            step(ev[s * L:(s + 1) * L])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
+        pre = np.mean([e[0].elapsed_time(e[1]) for e in ev])
+        scan = np.mean([e[1].elapsed_time(e[2]) for e in ev])
+        post = np.mean([e[2].elapsed_time(e[3]) for e in ev])
+        return dict(ms_per_step=total_ms / steps, pre_ms=pre, scan_ms=scan, post_ms=post)
+
+    log("timing fp16-output run")
+    r16 = run("f16", args.steps, args.warmup)
+    log("timing fp32-output run")
+    r32 = run("f32", args.steps, args.warmup)
+
+    scan_s = r16["scan_ms"] / 1e3
+    achieved_tf = scan_flops(T, hv) / scan_s / 1e12
+    traffic = load_traffic()
+    roof = {"bound": "alu", "achieved": round(achieved_tf, 3), "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved_tf / FP32_VECTOR_PEAK_TFLOPS, 4),
+            "traffic": traffic, "kernel": "gdn_scan",
+            "peak_unpacked_fp32": FP32_VECTOR_UNPACKED_TFLOPS,
+            "frac_of_unpacked": round(achieved_tf / FP32_VECTOR_UNPACKED_TFLOPS, 4)}
+
+    def stage_report(r, out_bytes):
+        return {
+            "pre_us": round(r["pre_ms"] * 1e3, 2),
+            "scan_us": round(r["scan_ms"] * 1e3, 2),
+            "post_us": round(r["post_ms"] * 1e3, 2),
+            "pre_hbm_frac": round(pre_bytes(T, hk, hv) / (r["pre_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "post_hbm_frac": round(post_bytes(T, hv, out_bytes=out_bytes) / (r["post_ms"] / 1e3)
+                                   / 1e9 / HBM_PEAK_GBS, 4),
+            "scan_tflops": round(scan_flops(T, hv) / (r["scan_ms"] / 1e3) / 1e12, 3),
+        }
+
+    res = {
+        "metric": METRIC,
+        "value": round(T / (r16["ms_per_step"] / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r16["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w16.name, "layers": L, "T": T, "batch": 1, "hk": hk, "hv": hv,
+                   "head_dim": 128, "io": "fp16", "state": "fp32", "out": "fp16",
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "stages_fp16_out": stage_report(r16, 2),
+        "fp32_out": {"value": round(T / (r32["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
+                     "ms_per_step": round(r32["ms_per_step"], 4), **stage_report(r32, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host cores")
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+// gdn_abi.hip -- the extern "C" entry points of include/gdn.h: argument
+// checks (all before anything is enqueued), then the stage launchers.
+#include <math.h>
+#include <stdint.h>
+
+#include "gdn_internal.h"
+
+namespace {
+
+using gdn::PreArgs;
+using gdn::ScanArgs;
+using gdn::PostArgs;
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 31;
+constexpr int kMaxHeads = 1 << 12;
+constexpr int kMaxSeqs = 1 << 20;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
+
+int check_shape(const gdn_shape *s)
+{
+    if (!s) return GDN_E_NULL;
+    if (s->io_dtype != GDN_F32 && s->io_dtype != GDN_F16) return GDN_E_DTYPE;
+    if (s->out_dtype != GDN_F32 && s->out_dtype != GDN_F16) return GDN_E_DTYPE;
+    if (s->dk != 128 || s->dv != 128) return GDN_E_SHAPE;
+    if (s->hk < 1 || s->hv < 1 || s->hk > kMaxHeads || s->hv > kMaxHeads) return GDN_E_SHAPE;
+    if (s->hv % s->hk != 0) return GDN_E_SHAPE;
+    if (s->n_seq < 1 || s->n_seq > kMaxSeqs) return GDN_E_SHAPE;
+    if (s->reserved != 0) return GDN_E_SHAPE;
+    if (s->total_T < 0 || s->total_T >= kMaxTokens) return GDN_E_SHAPE;
+    if (s->max_T < 0 || s->max_T > s->total_T) return GDN_E_SHAPE;
+    if (s->total_T > 0 && s->max_T < 1) return GDN_E_SHAPE;
+    if ((int64_t)s->n_seq * s->max_T < s->total_T) return GDN_E_SHAPE;
+    if (!finite_nonneg(s->eps_l2) || !finite_nonneg(s->eps_rms)) return GDN_E_SHAPE;
+    // launch-grid limits of the pre kernel (tile of 8 tokens at worst)
+    const int64_t pre_blocks = (int64_t)s->n_seq * ((s->max_T + 7) / 8);
+    if (pre_blocks >= ((int64_t)1 << 31)) return GDN_E_SHAPE;
+    return GDN_OK;
+}
+
+#define REQ(p)                                  \
+    do {                                        \
+        if (!(p)) return GDN_E_NULL;            \
+    } while (0)
+#define ALN(p, a)                               \
+    do {                                        \
+        if (!aligned((p), (a))) return GDN_E_ALIGN; \
+    } while (0)
+
+int check_pre(const gdn_shape *s, const int32_t *cu, const void *qkv, const void *conv_w,
+              const void *a, const void *b, const void *A_log, const void *dt_bias,
+              const void *hist, const float *qn, const float *kn, const float *vc,
+              const float *g, const float *beta)
+{
+    REQ(cu); REQ(qkv); REQ(conv_w); REQ(a); REQ(b); REQ(A_log); REQ(dt_bias); REQ(hist);
+    REQ(qn); REQ(kn); REQ(vc); REQ(g); REQ(beta);
+    ALN(cu, 4); ALN(a, 4); ALN(b, 4); ALN(A_log, 4); ALN(dt_bias, 4); ALN(g, 4); ALN(beta, 4);
+    ALN(qkv, 16); ALN(conv_w, 16); ALN(hist, 16); ALN(qn, 16); ALN(kn, 16); ALN(vc, 16);
+    return GDN_OK;
+}
+
+int check_scan(const int32_t *cu, const float *qn, const float *kn, const float *vc,
+               const float *g, const float *beta, const float *state, const float *o)
+{
+    REQ(cu); REQ(qn); REQ(kn); REQ(vc); REQ(g); REQ(beta); REQ(state); REQ(o);
+    ALN(cu, 4); ALN(g, 4); ALN(beta, 4);
+    ALN(qn, 16); ALN(kn, 16); ALN(vc, 16); ALN(state, 16); ALN(o, 16);
+    return GDN_OK;
+}
+
+int check_post(const float *o, const void *z, const void *gamma, const void *y)
+{
+    REQ(o); REQ(z); REQ(gamma); REQ(y);
+    ALN(o, 16); ALN(z, 16); ALN(gamma, 16); ALN(y, 16);
+    return GDN_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+    size_t qn, kn, vc, g, beta, o, total;
+};
+
+Carve carve(const gdn_shape *s)
+{
+    const size_t T = (size_t)s->total_T;
+    Carve c;
+    size_t off = 0;
+    c.qn = off; off += round256(T * s->hk * 128 * sizeof(float));
+    c.kn = off; off += round256(T * s->hk * 128 * sizeof(float));
+    c.vc = off; off += round256(T * s->hv * 128 * sizeof(float));
+    c.g = off; off += round256(T * s->hv * sizeof(float));
+    c.beta = off; off += round256(T * s->hv * sizeof(float));
+    c.o = off; off += round256(T * s->hv * 128 * sizeof(float));
+    c.total = off;
+    return c;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_LAUNCH; }
+
+} // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_str(int status)
+{
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_E_NULL: return "a required pointer is NULL";
+    case GDN_E_SHAPE: return "unsupported or inconsistent sizes";
+    case GDN_E_ALIGN: return "a pointer is not aligned as required";
+    case GDN_E_WORKSPACE: return "workspace too small";
+    case GDN_E_DTYPE: return "unknown dtype";
+    case GDN_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int gdn_pre(const gdn_shape *shape, const int32_t *cu_seqlens, const void *qkv,
+            const void *conv_w, const void *a, const void *b, const void *A_log,
+            const void *dt_bias, void *hist, float *qn, float *kn, float *vc, float *g,
+            float *beta, void *stream)
+{
+    int st = check_shape(shape);
+    if (st) return st;
+    if (shape->total_T == 0) return GDN_OK;
+    st = check_pre(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta);
+    if (st) return st;
+    const PreArgs pa{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta};
+    return launch_status(gdn::launch_pre(*shape, pa, (hipStream_t)stream));
+}
+
+int gdn_scan(const gdn_shape *shape, const int32_t *cu_seqlens, const float *qn,
+             const float *kn, const float *vc, const float *g, const float *beta,
+             float *state, float *o, void *stream)
+{
+    int st = check_shape(shape);
+    if (st) return st;
+    if (shape->total_T == 0) return GDN_OK;
+    st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o);
+    if (st) return st;
+    const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o};
+    return launch_status(gdn::launch_scan(*shape, sa, (hipStream_t)stream));
+}
+
+int gdn_post(const gdn_shape *shape, const float *o, const void *z, const void *gamma,
+             void *y, void *stream)
+{
+    int st = check_shape(shape);
+    if (st) return st;
+    if (shape->total_T == 0) return GDN_OK;
+    st = check_post(o, z, gamma, y);
+    if (st) return st;
+    const PostArgs pa{o, z, gamma, y};
+    return launch_status(gdn::launch_post(*shape, pa, (hipStream_t)stream));
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape)
+{
+    if (check_shape(shape) != GDN_OK) return 0;
+    return carve(shape).total;
+}
+
+int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const void *qkv,
+                      const void *conv_w, const void *a, const void *b, const void *A_log,
+                      const void *dt_bias, const void *z, const void *gamma, void *hist,
+                      float *state, void *y, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    int st = check_shape(shape);
+    if (st) return st;
+    if (shape->total_T == 0) return GDN_OK;
+    REQ(workspace);
+    ALN(workspace, 256);
+    const Carve c = carve(shape);
+    if (workspace_bytes < c.total) return GDN_E_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *qn = reinterpret_cast<float *>(ws + c.qn);
+    float *kn = reinterpret_cast<float *>(ws + c.kn);
+    float *vc = reinterpret_cast<float *>(ws + c.vc);
+    float *g = reinterpret_cast<float *>(ws + c.g);
+    float *beta = reinterpret_cast<float *>(ws + c.beta);
+    float *o = reinterpret_cast<float *>(ws + c.o);
+    st = check_pre(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta);
+    if (st) return st;
+    st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o);
+    if (st) return st;
+    st = check_post(o, z, gamma, y);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const PreArgs pa{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta};
+    if (gdn::launch_pre(*shape, pa, s) != hipSuccess) return GDN_E_LAUNCH;
+    const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o};
+    if (gdn::launch_scan(*shape, sa, s) != hipSuccess) return GDN_E_LAUNCH;
+    const PostArgs po{o, z, gamma, y};
+    return launch_status(gdn::launch_post(*shape, po, s));
+}
+
+} // extern "C"

@@ -1,0 +1,39 @@
+// gdn_internal.h -- launchers behind the C ABI (include/gdn.h).  Each one
+// assumes its arguments were validated by the ABI layer and only enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+struct PreArgs {
+    const int32_t *cu;
+    const void *qkv, *conv_w, *a, *b, *A_log, *dt_bias;
+    void *hist;
+    float *qn, *kn, *vc, *g, *beta;
+};
+
+struct ScanArgs {
+    const int32_t *cu;
+    const float *qn, *kn, *vc, *g, *beta;
+    float *state, *o;
+};
+
+struct PostArgs {
+    const float *o;
+    const void *z, *gamma;
+    void *y;
+};
+
+hipError_t launch_pre(const gdn_shape &s, const PreArgs &a, hipStream_t st);
+hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st);
+hipError_t launch_post(const gdn_shape &s, const PostArgs &a, hipStream_t st);
+
+// Grid-size limits the ABI checks before launching.
+constexpr int PRE_TILE_F16 = 16;  // tokens per pre tile, fp16 storage
+constexpr int PRE_TILE_F32 = 8;   // tokens per pre tile, fp32 storage
+
+} // namespace gdn

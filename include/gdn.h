@@ -1,0 +1,190 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet prefill path.
+ *
+ * Three stages, each a hand-written HIP kernel, plus the whole layer:
+ *
+ *   gdn_pre   4-tap causal depthwise conv over the packed q|k|v channels with
+ *             a carried 3-token history, SiLU, per-key-head L2 norm of q and
+ *             k, and the per-value-head decay and write-strength gates.
+ *   gdn_scan  the gated delta rule on a per-value-head fp32 state.
+ *   gdn_post  per-(token, value head) RMSNorm with gamma, times SiLU(z).
+ *   gdn_prefill_layer  pre -> scan -> post with the intermediates in a
+ *             caller-provided workspace.
+ *
+ * The stage split, the buffer set (q, k, v, gates, history, o, state, y)
+ * and the fp16/fp32 output switch are those of the audited Metal path:
+ * "Round 30 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", sections 1
+ * and 2 (the ten buffers checked per stage).  The production widths (16 key
+ * heads, 48 value heads, head dim 128, 10240 channels, eps 1e-6) are those of
+ * "round 10 track b: gdn vectorization and scan", "source and execution".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers are DEVICE pointers on the current HIP device, except `shape`,
+ * which is a host pointer read during the call only.  `stream` is a
+ * hipStream_t passed as void* (NULL = the default stream).  Every function only
+ * enqueues work on `stream`; none synchronises, allocates or keeps state, so
+ * calls are re-entrant.  The caller owns every buffer.
+ *
+ * Return value: GDN_OK (0), or a negative gdn_status.  All argument checks
+ * run before anything is enqueued, so on error nothing has been launched.
+ * Errors of the asynchronous kernels themselves surface at the caller's next
+ * synchronisation.  A call with total_T == 0 is a no-op that returns GDN_OK
+ * (history and state unchanged).
+ *
+ * Layouts (row-major).  C = 2*hk*dk + hv*dv.  "io" = shape->io_dtype.
+ *   cu_seqlens [n_seq+1] int32  sequence n owns tokens [cu[n], cu[n+1]);
+ *                               cu[0] = 0, non-decreasing, cu[n_seq] = total_T,
+ *                               and no sequence longer than max_T.  These
+ *                               device contents cannot be checked without a
+ *                               sync: they are a precondition.
+ *   qkv     [total_T][C]      io   channel blocks q | k | v; head i of a block
+ *                                  occupies channels [i*d, (i+1)*d)
+ *   conv_w  [C][4]            io   tap 3 multiplies the current token, tap 0
+ *                                  the token three steps back; no bias
+ *   a, b    [total_T][hv]     io   decay and write-strength logits
+ *   A_log, dt_bias [hv]       io
+ *   hist    [n_seq][3][C]     io   carried conv history, oldest row first
+ *   qn, kn  [total_T][hk][dk] fp32 normalised q, k
+ *   vc      [total_T][hv][dv] fp32 SiLU(conv) of the value channels
+ *   g, beta [total_T][hv]     fp32 log decay and write strength
+ *   state   [n_seq][hv][dv][dk] fp32  row index = value channel
+ *   o       [total_T][hv][dv] fp32 scan output
+ *   z       [total_T][hv][dv] io   output-gate input
+ *   gamma   [dv]              io   RMSNorm weight shared by all value heads
+ *   y       [total_T][hv][dv] shape->out_dtype
+ * Alignment: qkv, conv_w, hist, qn, kn, vc, state, o, z, gamma, y and the
+ * workspace must be 16-byte aligned; a, b, A_log, dt_bias, g, beta and
+ * cu_seqlens 4-byte aligned (GDN_E_ALIGN otherwise).
+ * No two buffers may overlap, except where an argument is documented as
+ * read-then-overwritten in place (hist, state).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_E_NULL = -1,      /* a required pointer is NULL                        */
+    GDN_E_SHAPE = -2,     /* unsupported or inconsistent sizes                 */
+    GDN_E_ALIGN = -3,     /* a pointer is not aligned as required              */
+    GDN_E_WORKSPACE = -4, /* workspace smaller than gdn_prefill_workspace_bytes */
+    GDN_E_DTYPE = -5,     /* io_dtype or out_dtype not a gdn_dtype             */
+    GDN_E_LAUNCH = -6     /* the HIP runtime rejected a kernel launch          */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,
+    GDN_F16 = 1
+} gdn_dtype;
+
+/* Sizes of one call.  Supported: dk = dv = 128, hk >= 1, hv >= 1,
+ * hv % hk == 0 (value head h reads key head h / (hv / hk)), n_seq >= 1,
+ * 0 <= max_T <= total_T < 2^31, max_T >= 1 when total_T >= 1.
+ * eps_l2 is added to the sum of squares inside the square root of the q/k
+ * L2 norm; eps_rms to the mean square inside that of the RMSNorm
+ * (both 1e-6 in the audited configuration; both must be finite and >= 0). */
+typedef struct gdn_shape {
+    int32_t hk, hv, dk, dv;
+    int32_t n_seq;
+    int32_t io_dtype;   /* gdn_dtype of qkv, conv_w, a, b, A_log, dt_bias, hist, z, gamma */
+    int32_t out_dtype;  /* gdn_dtype of y */
+    int32_t reserved;   /* must be 0 */
+    int64_t total_T;    /* = cu_seqlens[n_seq] */
+    int64_t max_T;      /* host copy of max_n (cu[n+1] - cu[n]) */
+    float eps_l2;
+    float eps_rms;
+} gdn_shape;
+
+/* ABI version this library implements (GDN_ABI_VERSION). */
+int gdn_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char *gdn_status_str(int status);
+
+/*
+ * gdn_pre -- "Round 30 Track C Audit", section 1 (gdn_pre): the 4-tap conv
+ * loop with the history paths for the first three tokens, the history write
+ * at the last token, and the per-key-head sums of squares; "round 10 track
+ * b", "variants": four ordered multiply-adds per element and SiLU on the value
+ * channels too.
+ *
+ * Per sequence n with T_n tokens let X = [hist[n]; qkv rows of n] ((3+T_n) x C):
+ *   x~[t][c] = sum_{m=0..3} conv_w[c][m] * X[t+m][c]
+ *   s = SiLU(x~) = x~ * sigmoid(x~)
+ *   qn = s_q / sqrt(|s_q|^2 + eps_l2) per key head, kn likewise, vc = s_v
+ *   g[t][h] = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h]); beta = sigmoid(b)
+ *   hist[n] <- X[T_n .. T_n+2]  (for T_n < 3 this keeps 3-T_n old rows)
+ * In:  cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist (read).
+ * Out: qn, kn, vc, g, beta; hist (overwritten in place after it is read).
+ */
+int gdn_pre(const gdn_shape *shape, const int32_t *cu_seqlens,
+            const void *qkv, const void *conv_w, const void *a, const void *b,
+            const void *A_log, const void *dt_bias, void *hist,
+            float *qn, float *kn, float *vc, float *g, float *beta,
+            void *stream);
+
+/*
+ * gdn_scan -- "Round 30 Track C Audit", section 1 (gdn_scan_r findings): a
+ * per-value-head state updated token by token in the loop that forms the dot
+ * products against the old state; section 2: a token-blocked run must equal
+ * the single pass.
+ *
+ * For each sequence n and value head h (key head j = h / (hv/hk)), over its
+ * tokens in order, with S the dv x dk state of (n, h):
+ *   alpha = exp(g[t][h])
+ *   S <- alpha*S + beta[t][h] * (vc[t][h] - alpha*S kn[t][j]) kn[t][j]^T
+ *   o[t][h] = S qn[t][j] / sqrt(dk)
+ * In:  cu_seqlens, qn, kn, vc, g, beta; state (read: S at the start).
+ * Out: o; state (overwritten in place with S after the last token).
+ * The result is bitwise independent of how a sequence is split across calls.
+ */
+int gdn_scan(const gdn_shape *shape, const int32_t *cu_seqlens,
+             const float *qn, const float *kn, const float *vc,
+             const float *g, const float *beta, float *state, float *o,
+             void *stream);
+
+/*
+ * gdn_post -- "Round 30 Track C Audit", section 1 (gdn_post): one sum of
+ * squares per row, gamma, and the fp16/fp32 output switch; "opus_r25_gdn --
+ * round 25 track A", "shipped": the sigmoid gate.
+ *
+ * For each (token, value head) row of dv values:
+ *   y_i = o_i / sqrt(mean_i(o_i^2) + eps_rms) * gamma_i * z_i * sigmoid(z_i)
+ * computed in fp32 and rounded to out_dtype (round to nearest even).
+ * In: o, z, gamma.  Out: y.
+ */
+int gdn_post(const gdn_shape *shape, const float *o, const void *z,
+             const void *gamma, void *y, void *stream);
+
+/* Bytes of workspace gdn_prefill_layer needs for `shape` (0 if the shape is
+ * invalid): room for qn, kn, vc, g, beta and o, each 256-byte aligned. */
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
+
+/*
+ * gdn_prefill_layer -- the three stages above in order on one stream, the
+ * whole path of one layer.  Arguments are those of gdn_pre, gdn_scan and
+ * gdn_post; the fp32 intermediates live in `workspace`
+ * (>= gdn_prefill_workspace_bytes(shape) bytes, device memory, contents
+ * undefined afterwards).  hist and state are read and overwritten in place.
+ */
+int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens,
+                      const void *qkv, const void *conv_w, const void *a,
+                      const void *b, const void *A_log, const void *dt_bias,
+                      const void *z, const void *gamma, void *hist,
+                      float *state, void *y, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

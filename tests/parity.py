@@ -1,0 +1,121 @@
+"""Comparison rules between the GPU path and the fp64 oracle.
+
+Bars (each written here once and used by every GPU test):
+- y stored as fp16: compared with the UNROUNDED fp64 oracle.  Where the fp16
+  half-spacing at y_ref is below 2e-3 (|y_ref| < 8) the error must be
+  <= 2e-3.  Above that no fp16 value can meet 2e-3, so the GPU value must be
+  one of the two fp16 neighbours of y_ref.
+- y stored as fp32: max |dy| <= 2e-3.
+- state: per (sequence, value head) ||S_gpu - S_ref||_F / ||S_ref||_F <= 1e-4.
+- o (fp32 scan output): the same 1e-4 relative Frobenius bar per value head.
+- history: bit-exact (a copy of stored input rows).
+- pre intermediates (fp32, one short fp32 chain per element): qn, kn, vc and
+  beta within 1e-5 relative + 1e-6 absolute; g (|g| up to ~80) 1e-5 relative.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Y_ABS = 2e-3
+STATE_REL = 1e-4
+O_REL = 1e-4
+PRE_RTOL, PRE_ATOL = 1e-5, 1e-6
+
+
+class ParityError(AssertionError):
+    pass
+
+
+def _fail(msg):
+    raise ParityError(msg)
+
+
+def fp16_neighbours(ref: np.ndarray):
+    r16 = ref.astype(np.float16)
+    up = np.nextafter(r16, np.float16(np.inf))
+    dn = np.nextafter(r16, np.float16(-np.inf))
+    lo = np.where(r16.astype(np.float64) <= ref, r16, dn)
+    hi = np.where(r16.astype(np.float64) >= ref, r16, up)
+    return lo, hi
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, out: str, what="y") -> dict:
+    """Returns a small report; raises ParityError on failure.  NaN in y_ref marks
+    elements the oracle did not compute (sampled checks)."""
+    ref = np.asarray(y_ref, np.float64).reshape(-1)
+    g = np.asarray(y_gpu).reshape(-1)
+    m = ~np.isnan(ref)
+    ref, g = ref[m], g[m]
+    if not np.isfinite(g.astype(np.float64)).all():
+        _fail(f"{what}: non-finite GPU values")
+    gd = g.astype(np.float64)
+    if out == "f32":
+        err = np.abs(gd - ref).max(initial=0.0)
+        if err > Y_ABS:
+            _fail(f"{what} fp32: max|dy| = {err:.3e} > {Y_ABS}")
+        return dict(n=int(ref.size), max_abs=float(err))
+    small = np.abs(ref) < 8.0
+    err_s = np.abs(gd[small] - ref[small]).max(initial=0.0)
+    if err_s > Y_ABS:
+        _fail(f"{what} fp16: max|dy| = {err_s:.3e} > {Y_ABS} where |y_ref| < 8")
+    big = ~small
+    n_big_bad = 0
+    if big.any():
+        lo, hi = fp16_neighbours(ref[big])
+        gb = g[big].astype(np.float16)
+        ok = (gb == lo) | (gb == hi)
+        n_big_bad = int((~ok).sum())
+        if n_big_bad:
+            _fail(f"{what} fp16: {n_big_bad} values with |y_ref| >= 8 are not an fp16 "
+                  f"neighbour of y_ref")
+    return dict(n=int(ref.size), max_abs_small=float(err_s), n_big=int(big.sum()))
+
+
+def rel_fro_per_head(x_gpu, x_ref, axes) -> np.ndarray:
+    d = np.asarray(x_gpu, np.float64) - x_ref
+    num = np.sqrt((d * d).sum(axis=axes))
+    den = np.sqrt((np.asarray(x_ref) ** 2).sum(axis=axes))
+    return num / np.maximum(den, 1e-300)
+
+
+def check_state(S_gpu, S_ref, heads=None) -> float:
+    """S: [n_seq, hv, dv, dk]."""
+    S_gpu, S_ref = np.asarray(S_gpu), np.asarray(S_ref)
+    if heads is not None:
+        S_gpu, S_ref = S_gpu[:, heads], S_ref[:, heads]
+    r = rel_fro_per_head(S_gpu, S_ref, axes=(2, 3))
+    zero = np.sqrt((np.asarray(S_ref) ** 2).sum(axis=(2, 3))) == 0
+    r = np.where(zero, np.abs(np.asarray(S_gpu, np.float64)).max(axis=(2, 3)), r)
+    worst = float(r.max(initial=0.0))
+    if not np.isfinite(worst) or worst > STATE_REL:
+        _fail(f"state: worst per-head relative Frobenius error {worst:.3e} > {STATE_REL}")
+    return worst
+
+
+def check_o(o_gpu, o_ref, heads=None) -> float:
+    """o: [T, hv, dv]; per value head over all tokens."""
+    o_gpu, o_ref = np.asarray(o_gpu), np.asarray(o_ref)
+    if heads is not None:
+        o_gpu, o_ref = o_gpu[:, heads], o_ref[:, heads]
+    r = rel_fro_per_head(o_gpu, o_ref, axes=(0, 2))
+    worst = float(r.max(initial=0.0))
+    if not np.isfinite(worst) or worst > O_REL:
+        _fail(f"o: worst per-head relative Frobenius error {worst:.3e} > {O_REL}")
+    return worst
+
+
+def check_close(name, gpu, ref, rtol=PRE_RTOL, atol=PRE_ATOL) -> float:
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(gpu - ref)
+    bad = err > atol + rtol * np.abs(ref)
+    if not np.isfinite(gpu).all() or bad.any():
+        i = np.argmax(err - rtol * np.abs(ref))
+        _fail(f"{name}: {int(bad.sum())} elements outside rtol={rtol} atol={atol}; worst "
+              f"gpu={gpu.reshape(-1)[i]!r} ref={ref.reshape(-1)[i]!r}")
+    return float(err.max(initial=0.0))
+
+
+def check_exact(name, gpu, ref):
+    if not np.array_equal(np.asarray(gpu), np.asarray(ref)):
+        _fail(f"{name}: not bit-exact")

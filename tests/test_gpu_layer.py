@@ -1,0 +1,154 @@
+"""Whole-layer parity (gdn_prefill_layer) against the fp64 oracle, on every
+workload: the tiny fp32 layer, the production-width T=512 layer, the 36-layer
+T=2048 stack (sampled: the launch the benchmark times, checked on chosen
+layers and value heads), the continuation sweep, and the long varlen batch.
+
+Also: bitwise determinism, and bitwise split invariance of the path ("Round
+30 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 2: the
+token-blocked scan must equal the single pass).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_pre_amd import binding as B
+from gated_deltanet_linear_pre_amd import synth
+from gated_deltanet_linear_pre_amd.buffers import LayerBuffers
+from oracle import gdn_oracle as orc
+
+from . import parity
+from .gpu_util import banner, np_
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _run_layer(w, inp, out=None, cu=None):
+    buf = LayerBuffers.create(w, inp, out=out, cu=cu)
+    ws = buf.workspace()
+    buf.run_layer(ws)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _check_layer(w, buf, ref, out, heads=None):
+    T = buf.shape.total_T
+    y = np_(buf.y).reshape(T, w.hv, 128)
+    y_ref = ref["y"]
+    if heads is not None:
+        y, y_ref = y[:, heads], y_ref[:, heads]
+    rep = parity.check_y(y, y_ref, out)
+    worst = parity.check_state(np_(buf.state), ref["S"], heads=heads)
+    parity.check_exact("hist", np_(buf.hist).astype(np.float64), ref["hist"])
+    return rep, worst
+
+
+@pytest.mark.parametrize("name", ["tiny_h2x6_t37_fp32", "prod_t512_fp16"])
+def test_layer_full_oracle(gpu, name):
+    w = W[name]
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", name)
+    buf = _run_layer(w, inp)
+    ref = orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp)
+    _check_layer(w, buf, ref, w.out)
+
+
+@pytest.mark.parametrize("name", ["prod36_t2048_fp16out", "prod36_t2048_fp32out"])
+@pytest.mark.parametrize("layer", [0, 35])
+def test_stack36_sampled_layers_and_heads(gpu, name, layer):
+    w = W[name]
+    heads = [0, 5, 24, 47]
+    inp = synth.layer_inputs(w, layer)
+    banner("gdn_prefill_layer", name, f"layer={layer}")
+    buf = _run_layer(w, inp)
+    ref = orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp, heads=heads)
+    _check_layer(w, buf, ref, w.out, heads=heads)
+
+
+def test_varlen_long_batch_sampled(gpu):
+    w = W["prod36_varlen4_fp32out"]
+    heads = [7, 40]
+    inp = synth.layer_inputs(w, 0)
+    banner("gdn_prefill_layer", w.name, "layer=0", f"lens={w.seqlens}")
+    buf = _run_layer(w, inp)
+    ref = orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp, heads=heads)
+    _check_layer(w, buf, ref, w.out, heads=heads)
+
+
+def test_continuation_split_equals_whole_and_oracle(gpu):
+    w = W["prod_continuation_fp16"]
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", w.name, "whole")
+    whole = _run_layer(w, inp)
+    ref = orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp)
+    _check_layer(w, whole, ref, w.out)
+
+    # the same tokens in segments 1, 3, 37, 300, 1024, carrying state and history
+    hist, state = inp["hist"], inp["S0"]
+    ys, s = [], 0
+    for L in w.segments:
+        part = dict(inp, hist=hist, S0=state)
+        for k in ("qkv", "a", "b", "z"):
+            part[k] = inp[k][s:s + L]
+        banner("gdn_prefill_layer", w.name, f"segment [{s}, {s + L})")
+        buf = _run_layer(w, part, cu=[0, L])
+        ys.append(np_(buf.y))
+        hist, state = np_(buf.hist), np_(buf.state)
+        s += L
+    assert np.array_equal(np.concatenate(ys), np_(whole.y)), "y differs between split and whole"
+    assert np.array_equal(state, np_(whole.state)), "state differs between split and whole"
+    assert np.array_equal(hist, np_(whole.hist)), "history differs between split and whole"
+
+
+def test_varlen_packing_equals_separate_calls(gpu):
+    # several sequences packed in one call == one call per sequence (bitwise),
+    # including empty sequences and ones shorter than the 3-token history
+    lens = (0, 1, 2, 3, 19, 0, 70)
+    w = synth.Workload("pack", hk=16, hv=48, seqlens=lens, seed=(12,), s0_std=0.05, hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", "varlen packed", f"lens={lens}")
+    packed = _run_layer(w, inp)
+    cu = w.cu_seqlens()
+    for n, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(np_(packed.state)[n], inp["S0"][n])
+            assert np.array_equal(np_(packed.hist)[n], inp["hist"][n])
+            continue
+        part = dict(inp, hist=inp["hist"][n:n + 1], S0=inp["S0"][n:n + 1])
+        for k in ("qkv", "a", "b", "z"):
+            part[k] = inp[k][cu[n]:cu[n + 1]]
+        banner("gdn_prefill_layer", "varlen single", f"seq={n}", f"T={L}")
+        one = _run_layer(w, part, cu=[0, L])
+        assert np.array_equal(np_(one.y), np_(packed.y)[cu[n]:cu[n + 1]])
+        assert np.array_equal(np_(one.state)[0], np_(packed.state)[n])
+        assert np.array_equal(np_(one.hist)[0], np_(packed.hist)[n])
+    ref = orc.layer(orc.Dims(w.hk, w.hv), cu, inp)
+    _check_layer(w, packed, ref, w.out)
+
+
+def test_layer_is_bitwise_deterministic(gpu):
+    w = W["prod_t512_fp16"]
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", "determinism")
+    a = _run_layer(w, inp)
+    b = _run_layer(w, inp)
+    assert np.array_equal(np_(a.y).view(np.uint16), np_(b.y).view(np.uint16))
+    assert np.array_equal(np_(a.state).view(np.uint32), np_(b.state).view(np.uint32))
+    assert np.array_equal(np_(a.hist).view(np.uint16), np_(b.hist).view(np.uint16))
+
+
+def test_stages_equal_layer_entry_point(gpu):
+    # gdn_pre + gdn_scan + gdn_post called one by one == gdn_prefill_layer (bitwise)
+    w = W["prod_t512_fp16"]
+    inp = synth.layer_inputs(w)
+    banner("gdn_pre/gdn_scan/gdn_post vs gdn_prefill_layer")
+    st = LayerBuffers.create(w, inp)
+    st.run_pre()
+    st.run_scan()
+    st.run_post()
+    torch.cuda.synchronize()
+    ly = _run_layer(w, inp)
+    assert np.array_equal(np_(st.y).view(np.uint16), np_(ly.y).view(np.uint16))
+    assert np.array_equal(np_(st.state), np_(ly.state))
+    assert np.array_equal(np_(st.hist), np_(ly.hist))
