@@ -74,33 +74,29 @@ def load_traffic():
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s=12.0):
-    """The fp64 oracle, as it stands, on a prefix of layer 0's tokens (all 48
-    heads, all three stages), doubling the prefix until a run takes ~1/3 of
-    the budget; reports tokens/s of the last run."""
+def cpu_baseline(budget_s=15.0, layers_total=36):
+    """The fp64 oracle, as it stands, on whole layers of the same workload
+    (T=2048, all 48 value heads, pre+scan+post), one layer after another until
+    ~budget_s of oracle time; tokens/s is scaled to the 36-layer pass the
+    metric counts (T / (mean seconds per layer x 36))."""
     import numpy as np
     from gated_deltanet_linear_pre_amd import synth
     from oracle import gdn_oracle as orc
 
     w = synth.WORKLOADS["prod36_t2048_fp16out"]
-    inp = synth.layer_inputs(w, 0)
     dims = orc.Dims(w.hk, w.hv)
-    n, spent, rate = 8, 0.0, None
-    while True:
-        part = dict(inp)
-        for k in ("qkv", "a", "b", "z"):
-            part[k] = inp[k][:n]
+    times = []
+    while len(times) < layers_total and sum(times) < budget_s:
+        inp = synth.layer_inputs(w, len(times))
         t0 = time.perf_counter()
-        orc.layer(dims, np.array([0, n]), part)
-        dt = time.perf_counter() - t0
-        spent += dt
-        rate = n / dt
-        if dt > budget_s / 3 or n >= w.total_T or spent > budget_s:
-            break
-        n = min(2 * n, w.total_T)
-    return dict(value=rate, unit="tokens/s", cores=orc.max_threads(), kind="oracle",
-                sample=f"layer 0 of the 36-layer T=2048 workload, first {n} tokens, all 48 value "
-                       f"heads, pre+scan+post in fp64 ({dt:.1f} s for that run)")
+        orc.layer(dims, w.cu_seqlens(), inp)
+        times.append(time.perf_counter() - t0)
+    per_layer = float(np.mean(times))
+    return dict(value=round(w.total_T / (per_layer * layers_total), 2), unit="tokens/s",
+                cores=orc.max_threads(), kind="oracle",
+                sample=f"{len(times)} of the 36 layers (layers 0..{len(times) - 1}), each full "
+                       f"T=2048, all 48 value heads, pre+scan+post in fp64; "
+                       f"{per_layer:.2f} s per layer, scaled to 36 layers")
 
 
 def main():
