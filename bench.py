@@ -147,11 +147,13 @@ def main():
     g = torch.empty((T, hv), **f32)
     beta = torch.empty((T, hv), **f32)
     o = torch.empty((T, hv, 128), **f32)
+    from gated_deltanet_linear_pre_amd.buffers import scratch
     stream = torch.cuda.current_stream()
 
     def run(out, steps, warmup):
         ys = [torch.empty((T, hv * 128), dtype=TORCH_DTYPE[out], device=dev) for _ in range(L)]
         shape = B.make_shape(hk, hv, 1, T, T, io="f16", out=out)
+        sws = scratch(B.gdn_scan_workspace_bytes(shape), dev)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L * steps)]
 
         def step(events=None):
@@ -161,7 +163,7 @@ def main():
                 B.gdn_pre(shape, cu, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"],
                           d["dt_bias"], d["hist"], qn, kn, vc, g, beta, stream=stream)
                 if e: e[1].record(stream)
-                B.gdn_scan(shape, cu, qn, kn, vc, g, beta, d["S0"], o, stream=stream)
+                B.gdn_scan(shape, cu, qn, kn, vc, g, beta, d["S0"], o, sws, stream=stream)
                 if e: e[2].record(stream)
                 B.gdn_post(shape, o, d["z"], d["gamma"], ys[l], stream=stream)
                 if e: e[3].record(stream)

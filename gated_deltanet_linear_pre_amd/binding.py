@@ -63,7 +63,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_pre.restype = I
         L.gdn_pre.argtypes = [SP] + [P] * 14
         L.gdn_scan.restype = I
-        L.gdn_scan.argtypes = [SP] + [P] * 9
+        L.gdn_scan.argtypes = [SP] + [P] * 9 + [S, P]
+        L.gdn_scan_workspace_bytes.restype = S
+        L.gdn_scan_workspace_bytes.argtypes = [SP]
         L.gdn_post.restype = I
         L.gdn_post.argtypes = [SP] + [P] * 5
         L.gdn_prefill_workspace_bytes.restype = S
@@ -120,9 +122,17 @@ def gdn_pre(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, 
     return st
 
 
-def gdn_scan(shape, cu_seqlens, qn, kn, vc, g, beta, state, o, stream=None, check=True) -> int:
-    st = lib().gdn_scan(ctypes.byref(shape), *map(_ptr, (cu_seqlens, qn, kn, vc, g, beta, state, o)),
-                        _stream(stream))
+def gdn_scan_workspace_bytes(shape) -> int:
+    return int(lib().gdn_scan_workspace_bytes(ctypes.byref(shape)))
+
+
+def gdn_scan(shape, cu_seqlens, qn, kn, vc, g, beta, state, o, workspace, workspace_bytes=None,
+             stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().gdn_scan(ctypes.byref(shape), *map(_ptr, (cu_seqlens, qn, kn, vc, g, beta, state, o,
+                                                            workspace)),
+                        int(workspace_bytes), _stream(stream))
     if check:
         _check("gdn_scan", st)
     return st

@@ -15,6 +15,14 @@ from . import binding
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16}
 
 
+def scratch(nbytes: int, device) -> torch.Tensor:
+    """Device scratch of at least nbytes, 256-byte aligned (torch's caching
+    allocator hands out blocks aligned to at least 512 bytes)."""
+    t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
 def upload(arr: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
 
@@ -71,16 +79,19 @@ class LayerBuffers:
                         self.dt_bias, self.hist, self.qn, self.kn, self.vc, self.g, self.beta,
                         stream=stream)
 
-    def run_scan(self, stream=None):
+    def scan_workspace(self) -> torch.Tensor:
+        return scratch(binding.gdn_scan_workspace_bytes(self.shape), self.qkv.device)
+
+    def run_scan(self, workspace=None, stream=None):
+        ws = self.scan_workspace() if workspace is None else workspace
         binding.gdn_scan(self.shape, self.cu, self.qn, self.kn, self.vc, self.g, self.beta,
-                         self.state, self.o, stream=stream)
+                         self.state, self.o, ws, stream=stream)
 
     def run_post(self, stream=None):
         binding.gdn_post(self.shape, self.o, self.z, self.gamma, self.y, stream=stream)
 
     def workspace(self) -> torch.Tensor:
-        nbytes = binding.gdn_prefill_workspace_bytes(self.shape)
-        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.qkv.device)
+        return scratch(binding.gdn_prefill_workspace_bytes(self.shape), self.qkv.device)
 
     def run_layer(self, workspace: torch.Tensor, stream=None):
         binding.gdn_prefill_layer(self.shape, self.cu, self.qkv, self.conv_w, self.a, self.b,

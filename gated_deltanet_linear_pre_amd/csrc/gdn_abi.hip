@@ -34,9 +34,10 @@ int check_shape(const gdn_shape *s)
     if (s->total_T > 0 && s->max_T < 1) return GDN_E_SHAPE;
     if ((int64_t)s->n_seq * s->max_T < s->total_T) return GDN_E_SHAPE;
     if (!finite_nonneg(s->eps_l2) || !finite_nonneg(s->eps_rms)) return GDN_E_SHAPE;
-    // launch-grid limits of the pre kernel (tile of 8 tokens at worst)
+    // launch-grid limits (pre: tiles of 8 tokens at worst; scan prep: 16)
     const int64_t pre_blocks = (int64_t)s->n_seq * ((s->max_T + 7) / 8);
     if (pre_blocks >= ((int64_t)1 << 31)) return GDN_E_SHAPE;
+    if ((int64_t)s->n_seq * s->hv * 4 >= ((int64_t)1 << 31)) return GDN_E_SHAPE;
     return GDN_OK;
 }
 
@@ -62,11 +63,12 @@ int check_pre(const gdn_shape *s, const int32_t *cu, const void *qkv, const void
 }
 
 int check_scan(const int32_t *cu, const float *qn, const float *kn, const float *vc,
-               const float *g, const float *beta, const float *state, const float *o)
+               const float *g, const float *beta, const float *state, const float *o,
+               const void *ws)
 {
-    REQ(cu); REQ(qn); REQ(kn); REQ(vc); REQ(g); REQ(beta); REQ(state); REQ(o);
+    REQ(cu); REQ(qn); REQ(kn); REQ(vc); REQ(g); REQ(beta); REQ(state); REQ(o); REQ(ws);
     ALN(cu, 4); ALN(g, 4); ALN(beta, 4);
-    ALN(qn, 16); ALN(kn, 16); ALN(vc, 16); ALN(state, 16); ALN(o, 16);
+    ALN(qn, 16); ALN(kn, 16); ALN(vc, 16); ALN(state, 16); ALN(o, 16); ALN(ws, 256);
     return GDN_OK;
 }
 
@@ -80,7 +82,7 @@ int check_post(const float *o, const void *z, const void *gamma, const void *y)
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t qn, kn, vc, g, beta, o, total;
+    size_t qn, kn, vc, g, beta, o, scan, total;
 };
 
 Carve carve(const gdn_shape *s)
@@ -94,6 +96,7 @@ Carve carve(const gdn_shape *s)
     c.g = off; off += round256(T * s->hv * sizeof(float));
     c.beta = off; off += round256(T * s->hv * sizeof(float));
     c.o = off; off += round256(T * s->hv * 128 * sizeof(float));
+    c.scan = off; off += round256(gdn::scan_workspace_bytes(*s));
     c.total = off;
     return c;
 }
@@ -134,16 +137,23 @@ int gdn_pre(const gdn_shape *shape, const int32_t *cu_seqlens, const void *qkv,
     return launch_status(gdn::launch_pre(*shape, pa, (hipStream_t)stream));
 }
 
+size_t gdn_scan_workspace_bytes(const gdn_shape *shape)
+{
+    if (check_shape(shape) != GDN_OK) return 0;
+    return gdn::scan_workspace_bytes(*shape);
+}
+
 int gdn_scan(const gdn_shape *shape, const int32_t *cu_seqlens, const float *qn,
              const float *kn, const float *vc, const float *g, const float *beta,
-             float *state, float *o, void *stream)
+             float *state, float *o, void *workspace, size_t workspace_bytes, void *stream)
 {
     int st = check_shape(shape);
     if (st) return st;
     if (shape->total_T == 0) return GDN_OK;
-    st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o);
+    st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o, workspace);
     if (st) return st;
-    const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o};
+    if (workspace_bytes < gdn::scan_workspace_bytes(*shape)) return GDN_E_WORKSPACE;
+    const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o, static_cast<float *>(workspace)};
     return launch_status(gdn::launch_scan(*shape, sa, (hipStream_t)stream));
 }
 
@@ -185,16 +195,17 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     float *g = reinterpret_cast<float *>(ws + c.g);
     float *beta = reinterpret_cast<float *>(ws + c.beta);
     float *o = reinterpret_cast<float *>(ws + c.o);
+    float *sws = reinterpret_cast<float *>(ws + c.scan);
     st = check_pre(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta);
     if (st) return st;
-    st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o);
+    st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o, sws);
     if (st) return st;
     st = check_post(o, z, gamma, y);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     const PreArgs pa{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta};
     if (gdn::launch_pre(*shape, pa, s) != hipSuccess) return GDN_E_LAUNCH;
-    const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o};
+    const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o, sws};
     if (gdn::launch_scan(*shape, sa, s) != hipSuccess) return GDN_E_LAUNCH;
     const PostArgs po{o, z, gamma, y};
     return launch_status(gdn::launch_post(*shape, po, s));

@@ -20,7 +20,12 @@ struct ScanArgs {
     const int32_t *cu;
     const float *qn, *kn, *vc, *g, *beta;
     float *state, *o;
+    float *ws;  // per-(chunk, value head) prep slots
 };
+
+// floats per (16-token chunk, value head) slot of the scan workspace
+constexpr int SCAN_SLOT_FLOATS = 640;
+size_t scan_workspace_bytes(const gdn_shape &s);
 
 struct PostArgs {
     const float *o;

@@ -1,213 +1,398 @@
-// gdn_scan.hip -- the gated delta rule, recurrent form, on an fp32 state.
+// gdn_scan.hip -- the gated delta rule on an fp32 state, in 16-token chunks on
+// fp32 MFMA.
 //
 // "Round 30 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 1
-// (gdn_scan_r findings): one state per value head, kept on chip and updated
-// token by token in the same pass that forms the dot products against the old
-// state; loads for the next tokens are issued before the per-token barrier.
-// Section 2: a token-blocked run must equal the single pass.
+// (gdn_scan_r findings): one state per value head, updated token by token in
+// the same pass that forms the dot products against the old state; section 2:
+// a token-blocked run must equal the single pass.
 //
-// For value head h (key head j = h / G) and its dv x dk state S, per token:
-//   alpha = exp(g),  p = S k,  r = S q                 (old state)
-//   u = beta (v - alpha p)
-//   S <- alpha S + u k^T
-//   o = (alpha r + u (k . q)) / sqrt(dk)   (= S_new q / sqrt(dk))
-// The last line is the plain o = S_t q / sqrt(dk), rewritten so that both dot
-// products use the old state in one pass.
+// The recurrence, per value head h (key head j = h / G), state S (dv x dk):
+//   S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,
+//   o_t = S_t q_t / sqrt(dk),  alpha_t = exp(g_t).
+// Over a chunk of C = 16 tokens starting from state S0, with
+//   D[t][s] = exp(g_{s+1} + ... + g_t)    (decay from just after s to t, <= 1)
+//   Lam_t   = exp(g_0 + ... + g_t)        (decay from the chunk start)
+// the writes u_t = beta_t (v_t - alpha_t S_{t-1} k_t) solve a unit lower
+// triangular system, and the outputs and the next state follow:
+//   (I + A) U = diag(beta) (V - diag(Lam) P),  A[t][s] = beta_t D[t][s] k_t.k_s (s<t)
+//   O  = diag(Lam) R + M U,                     M[t][s] = D[t][s] q_t.k_s     (s<=t)
+//   S' = Lam_last S0 + sum_s D[last][s] u_s k_s^T
+// with P = K S0^T, R = Q S0^T (tokens x value channels).  This is exact
+// algebra of the recurrence (unroll S_t = Lam_t S0 + sum_{s<=t} D[t][s] u_s k_s^T).
+// Every decay is formed as exp of a sum of at most 16 log decays, never as a
+// ratio of two cumulative products, so nothing overflows or cancels.
 //
-// gfx950 mapping.  Rows of S (value channels) evolve independently given the
-// token's k, q, alpha, beta, so the state is split by rows across the whole
-// chip.  A block of 4 waves owns 16 rows of one (sequence, value head).  A
-// 16-lane DPP row holds one state row, 8 key columns per lane, in registers.
-// The two row dot products are 8 FMAs per lane plus a 4-step DPP rotate-add,
-// with no LDS round trip and no barrier per token.  Tokens are staged through
-// LDS 16 at a time (k, q, the block's 16 v values, alpha, beta and k.q); the
-// next chunk's global loads are issued before the current chunk is computed.
-// So there are two barriers per 16 tokens rather than one per token.
-// Outputs collect in LDS and leave as one 64-byte store per token.
+// gfx950 mapping.
+// * gdn_scan_prep (fully parallel over sequence x chunk x key head): k.k and
+//   q.k of the chunk on MFMA (once per key head, shared by its G value heads),
+//   then per value head the decays, T = (I + A)^-1 by forward substitution (one
+//   column per lane, in registers), M, Lam, beta and the last-row decays.  The
+//   result goes to one slot per (chunk, value head) of the workspace.
+// * gdn_scan_chunk (sequential over chunks): a block of 4 waves owns 32 value
+//   channels of one (sequence, value head).  Each wave holds a 16-channel x
+//   64-key quarter of the state in MFMA accumulator layout (16 VGPRs/lane).
+//   Per chunk: K S0^T and Q S0^T over the wave's 64 keys (32 MFMA
+//   16x16x4 f32), the partial sums of the two key halves exchanged through
+//   LDS, U = T B (4 MFMA), O = Lam R + M U (4 MFMA, one wave per pair), and the
+//   state update Lam_last S0 + (D K)^T U (16 MFMA).  The state never leaves
+//   registers, and every product consumes the accumulator layout the previous
+//   one produced: the contraction index is permuted consistently, so no
+//   transposes are needed.
+//   The next chunk's K, Q, V and prep slot are loaded into registers while the
+//   current chunk computes.
+// * Block order is XCD-aware (blocks are dealt round-robin to the 8 XCDs; the
+//   index is permuted so each XCD gets whole heads and whole key-head groups,
+//   sharing their K/Q stream in one L2).
 //
-// Block order is XCD-aware: blocks are dealt round-robin to the 8 XCDs, so the
-// block index is permuted to give each XCD a contiguous run of
-// (sequence, head, row block) work items.  The 8 row blocks of a head then
-// share the key/query stream in one L2.
-//
-// Determinism: fixed-order FMAs and DPP trees, no atomics.  A sequence's
-// result does not depend on how it is split across calls (the state is
-// reloaded exactly as stored).
+// Determinism: fixed-order MFMA chains, no atomics; the two waves of a
+// channel block add the key halves in the same order, so they agree bit for
+// bit.  Splitting a sequence at a multiple of 16 tokens gives bit-identical
+// results; other split points agree within rounding (the chunk grid moves).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
 
-constexpr int SCAN_CT = 16;  // tokens per LDS chunk
-constexpr int SCAN_RB = 16;  // state rows per block
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-struct ScanDims {
-    int hk, hv, G;
-    int blocks_per_head;  // 128 / SCAN_RB
+constexpr int CT = 16;    // tokens per chunk
+constexpr int KS = 132;   // LDS row stride of the K/Q chunk (padded)
+// prep slot layout (floats)
+constexpr int OFF_T = 0;      // T = (I + A)^-1, [t][s]
+constexpr int OFF_M = 256;    // M / sqrt(dk), [t][s]
+constexpr int OFF_LAM = 512;  // Lam_t
+constexpr int OFF_LAMS = 528; // Lam_t / sqrt(dk)
+constexpr int OFF_BETA = 544; // beta_t (0 past the chunk's end)
+constexpr int OFF_W = 560;    // D[last][s] (0 past the end)
+constexpr int OFF_LAST = 576; // Lam_last
+static_assert(SCAN_SLOT_FLOATS >= 580 && SCAN_SLOT_FLOATS % 4 == 0, "slot too small");
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c)
+{
+    // D[i][j] += sum_k A[i][k] B[k][j], 16x16x4: lane l supplies A[l%16][l/16]
+    // and B[l/16][l%16]; D[4(l/16)+r][l%16] comes back in component r.
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Workspace slot of chunk c of sequence n (cu0 = cu[n]); injective, and
+// below total_T / 16 + n_seq.
+__device__ __forceinline__ int64_t chunk_slot(int cu0, int n, int c)
+{
+    return (int64_t)(cu0 >> 4) + c + n;
+}
+
+struct PrepDims {
+    int hk, hv, G, n_chunk_max;
 };
 
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs p, ScanDims d)
+__global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 {
-    __shared__ __attribute__((aligned(16))) float sk[SCAN_CT][128];
-    __shared__ __attribute__((aligned(16))) float sq[SCAN_CT][128];
-    __shared__ __attribute__((aligned(16))) float sv[SCAN_CT][SCAN_RB];
-    __shared__ __attribute__((aligned(16))) float so[SCAN_CT][SCAN_RB];
-    __shared__ __attribute__((aligned(16))) float spar[SCAN_CT][4];  // alpha, beta, k.q, unused
+    __shared__ __attribute__((aligned(16))) float sK[CT][KS];
+    __shared__ __attribute__((aligned(16))) float sQ[CT][KS];
+    __shared__ float sKK[CT][CT + 1];
+    __shared__ float sQK[CT][CT + 1];
+    __shared__ float sA[4][CT][CT + 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int l16 = lane & 15;
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
+    const int n = blockIdx.x / d.n_chunk_max;
+    const int c = blockIdx.x - n * d.n_chunk_max;
+    const int j = blockIdx.y;
+    const int cu0 = p.cu[n];
+    const int T_n = p.cu[n + 1] - cu0;
+    if (c * CT >= T_n) return;
+    const int nv = min(CT, T_n - c * CT);
+    const int64_t tb = (int64_t)cu0 + c * CT;
+    const int hk = d.hk, hv = d.hv;
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    // XCD-aware work index
+    // stage the chunk's k and q rows of key head j (zero past the end)
+#pragma unroll
+    for (int f2 = 0; f2 < 2; ++f2) {
+        const int f = tid + 256 * f2;
+        const int t = f >> 5, col = (f & 31) * 4;
+        const int tc = min(t, nv - 1);
+        const int64_t off = ((tb + tc) * hk + j) * 128 + col;
+        const f4 kv = *reinterpret_cast<const f4 *>(p.kn + off);
+        const f4 qv = *reinterpret_cast<const f4 *>(p.qn + off);
+        *reinterpret_cast<f4 *>(&sK[t][col]) = t < nv ? kv : z4;
+        *reinterpret_cast<f4 *>(&sQ[t][col]) = t < nv ? qv : z4;
+    }
+    __syncthreads();
+
+    // wave 0: K K^T, wave 1: Q K^T (16 x 16 over 128 keys, 32 MFMA each)
+    if (wave < 2) {
+        const float(*X)[KS] = wave == 0 ? sK : sQ;
+        f4 acc = z4;
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+            const f4 xa = *reinterpret_cast<const f4 *>(&X[l16][16 * jb + 4 * kk]);
+            const f4 kb = *reinterpret_cast<const f4 *>(&sK[l16][16 * jb + 4 * kk]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc = mfma4(xa[r], kb[r], acc);
+        }
+        float(*O)[CT + 1] = wave == 0 ? sKK : sQK;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[4 * kk + r][l16] = acc[r];
+    }
+    __syncthreads();
+
+    const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+    for (int gh = wave; gh < d.G; gh += 4) {
+        const int h = j * d.G + gh;
+        float *slot = p.ws + (chunk_slot(cu0, n, c) * hv + h) * SCAN_SLOT_FLOATS;
+        float gv[CT], bv[CT];
+#pragma unroll
+        for (int t = 0; t < CT; ++t) {
+            const int tc = min(t, nv - 1);
+            const float gg = p.g[(tb + tc) * hv + h];
+            const float bb = p.beta[(tb + tc) * hv + h];
+            gv[t] = t < nv ? gg : 0.f;
+            bv[t] = t < nv ? bb : 0.f;
+        }
+        // A (to LDS) and M (to the slot): entry (t, s), four per lane
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = lane + 64 * m;
+            const int t = e >> 4, s = e & 15;
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 1; r < CT; ++r)
+                if (r > s && r <= t) sum += gv[r];
+            const float dec = expf(sum);
+            const bool live = t < nv;
+            sA[wave][t][s] = (live && s < t) ? bv[t] * dec * sKK[t][s] : 0.f;
+            slot[OFF_M + e] = (live && s <= t) ? dec * sQK[t][s] * scale : 0.f;
+        }
+        if (lane < CT) {
+            const int t = lane;
+            float lam = 0.f, wdec = 0.f;
+#pragma unroll
+            for (int r = 0; r < CT; ++r) {
+                if (r <= t) lam += gv[r];
+                if (r > t && r < nv) wdec += gv[r];
+            }
+            const float L = t < nv ? expf(lam) : 0.f;
+            slot[OFF_LAM + t] = L;
+            slot[OFF_LAMS + t] = L * scale;
+            slot[OFF_BETA + t] = bv[t];
+            slot[OFF_W + t] = t < nv ? expf(wdec) : 0.f;
+            if (t == nv - 1) slot[OFF_LAST] = L;
+        }
+        // the wave's A writes must land before its lanes read them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < CT) {
+            // T = (I + A)^-1 by forward substitution; lane s keeps column s
+            const int s = lane;
+            float Tc[CT];
+#pragma unroll
+            for (int t = 0; t < CT; ++t) {
+                float acc = (t == s) ? 1.f : 0.f;
+#pragma unroll
+                for (int r = 0; r < t; ++r) acc = fmaf(-sA[wave][t][r], Tc[r], acc);
+                Tc[t] = acc;
+            }
+#pragma unroll
+            for (int t = 0; t < CT; ++t) slot[OFF_T + t * CT + s] = Tc[t];
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+struct ChunkDims {
+    int hk, hv, G;
+};
+
+__global__ __launch_bounds__(256) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
+{
+    __shared__ __attribute__((aligned(16))) float sK[CT][KS];
+    __shared__ __attribute__((aligned(16))) float sQ[CT][KS];
+    __shared__ __attribute__((aligned(16))) float sVT[32][20];  // v, [channel][token]
+    __shared__ __attribute__((aligned(16))) float sP[SCAN_SLOT_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sX[4][2][64][4];  // partial P, R
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
+
+    // XCD-aware work index -> (sequence n, value head h, 32-channel block rb)
     const int nb = gridDim.x;
     int w = (int)blockIdx.x;
     if ((nb & 7) == 0) w = (w & 7) * (nb >> 3) + (w >> 3);
-    const int rb = w % d.blocks_per_head;
-    w /= d.blocks_per_head;
+    const int rb = w & 3;
+    w >>= 2;
     const int h = w % d.hv;
     const int n = w / d.hv;
     const int j = h / d.G;
+    const int hk = d.hk, hv = d.hv;
 
-    const int64_t s0 = p.cu[n];
-    const int T_n = p.cu[n + 1] - p.cu[n];
+    const int cu0 = p.cu[n];
+    const int T_n = p.cu[n + 1] - cu0;
     if (T_n <= 0) return;
 
-    const int rl = (tid >> 6) * 4 + (lane >> 4);  // local row 0..15
-    const int row = rb * SCAN_RB + rl;
-    const int j0 = l16 * 8;
-    const int hv = d.hv, hk = d.hk;
-    const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+    const int rs = wave >> 1;  // 16-channel sub-block
+    const int jh = wave & 1;   // key half: key blocks 4 jh .. 4 jh + 3
+    const int row = rb * 32 + rs * 16 + l16;
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    float S[8];
-    float *Sp = p.state + (((int64_t)n * hv + h) * 128 + row) * 128 + j0;
-    load8(Sp, S);
+    // state quarter, accumulator layout: S4[b][r] = S[row][16 (4 jh + b) + 4 kk + r]
+    float *Srow = p.state + (((int64_t)n * hv + h) * 128 + row) * 128 + 64 * jh + 4 * kk;
+    f4 S4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b);
 
-    // staging roles: float4 f = tid and tid + 256 of the chunk's k and q
-    // (token f / 32, columns 4 (f % 32) ..); v: tid < 64 -> token tid / 4,
-    // rows 4 (tid % 4) ..; alpha/beta: tid < 16 -> token tid.
-    const int tokA = tid >> 5, tokB = tokA + 8;
-    const int colK = (tid & 31) * 4;
-    const int tokV = tid >> 2, colV = (tid & 3) * 4;
-    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 rkA = zero4, rkB = zero4, rqA = zero4, rqB = zero4, rv = zero4;
-    float rg = 0.f, rbeta = 0.f;
+    // staging roles (next chunk prefetched into registers): k and q rows by
+    // all 256 threads, v by threads 0..127, the prep slot (160 float4) by
+    // threads 96..255
+    constexpr int SLOT_T0 = 256 - SCAN_SLOT_FLOATS / 4;
+    static_assert(SLOT_T0 >= 0, "prep slot larger than one float4 per thread");
+    const int tA = tid >> 5, tB = tA + 8, colK = (tid & 31) * 4;
+    const int tV = tid >> 3, chV = (tid & 7) * 4;  // tid < 128
+    f4 rkA = z4, rkB = z4, rqA = z4, rqB = z4, rv = z4, rp = z4;
 
-#define GDN_SCAN_FETCH(c)                                                              \
+#define GDN_CHUNK_FETCH(c_)                                                            \
     do {                                                                               \
-        const int64_t tb_ = s0 + (int64_t)(c) * SCAN_CT;                               \
-        const int nv_ = min(SCAN_CT, T_n - (c) * SCAN_CT);                             \
+        const int64_t tb_ = (int64_t)cu0 + (int64_t)(c_) * CT;                         \
+        const int nv_ = min(CT, T_n - (c_) * CT);                                      \
+        const int64_t ks_ = (int64_t)hk * 128;                                         \
         const float *kb_ = p.kn + (tb_ * hk + j) * 128 + colK;                         \
         const float *qb_ = p.qn + (tb_ * hk + j) * 128 + colK;                         \
-        const int64_t tstr_ = (int64_t)hk * 128;                                       \
-        /* clamp to a valid token, then zero the value: no pointer select */         \
-        const int ta_ = min(tokA, nv_ - 1), tb2_ = min(tokB, nv_ - 1);                 \
-        const float4 ka_ = *reinterpret_cast<const float4 *>(kb_ + ta_ * tstr_);        \
-        const float4 qa_ = *reinterpret_cast<const float4 *>(qb_ + ta_ * tstr_);        \
-        const float4 kb2_ = *reinterpret_cast<const float4 *>(kb_ + tb2_ * tstr_);      \
-        const float4 qb2_ = *reinterpret_cast<const float4 *>(qb_ + tb2_ * tstr_);      \
-        rkA = tokA < nv_ ? ka_ : zero4;                                                \
-        rqA = tokA < nv_ ? qa_ : zero4;                                                \
-        rkB = tokB < nv_ ? kb2_ : zero4;                                               \
-        rqB = tokB < nv_ ? qb2_ : zero4;                                               \
-        if (tid < 64 && tokV < nv_)                                                    \
-            rv = *reinterpret_cast<const float4 *>(p.vc + ((tb_ + tokV) * hv + h) * 128 + \
-                                                   rb * SCAN_RB + colV);               \
-        if (tid < nv_) {                                                               \
-            rg = p.g[(tb_ + tid) * hv + h];                                            \
-            rbeta = p.beta[(tb_ + tid) * hv + h];                                      \
+        const int ta_ = min(tA, nv_ - 1), tb2_ = min(tB, nv_ - 1);                     \
+        const f4 k0_ = *reinterpret_cast<const f4 *>(kb_ + ta_ * ks_);                 \
+        const f4 q0_ = *reinterpret_cast<const f4 *>(qb_ + ta_ * ks_);                 \
+        const f4 k1_ = *reinterpret_cast<const f4 *>(kb_ + tb2_ * ks_);                \
+        const f4 q1_ = *reinterpret_cast<const f4 *>(qb_ + tb2_ * ks_);                \
+        rkA = tA < nv_ ? k0_ : z4;                                                     \
+        rqA = tA < nv_ ? q0_ : z4;                                                     \
+        rkB = tB < nv_ ? k1_ : z4;                                                     \
+        rqB = tB < nv_ ? q1_ : z4;                                                     \
+        if (tid < 128) {                                                               \
+            const f4 v_ = *reinterpret_cast<const f4 *>(                               \
+                p.vc + ((tb_ + min(tV, nv_ - 1)) * hv + h) * 128 + rb * 32 + chV);     \
+            rv = tV < nv_ ? v_ : z4;                                                   \
         }                                                                              \
+        if (tid >= SLOT_T0)                                                            \
+            rp = *reinterpret_cast<const f4 *>(                                        \
+                p.ws + (chunk_slot(cu0, n, (c_)) * hv + h) * SCAN_SLOT_FLOATS +         \
+                4 * (tid - SLOT_T0));                                                  \
     } while (0)
 
-#define GDN_SCAN_FLUSH(c)                                                              \
-    do {                                                                               \
-        const int64_t tb_ = s0 + (int64_t)(c) * SCAN_CT;                               \
-        const int nv_ = min(SCAN_CT, T_n - (c) * SCAN_CT);                             \
-        if (tid < 64 && tokV < nv_)                                                    \
-            *reinterpret_cast<float4 *>(p.o + ((tb_ + tokV) * hv + h) * 128 +          \
-                                        rb * SCAN_RB + colV) =                         \
-                *reinterpret_cast<const float4 *>(&so[tokV][colV]);                    \
-    } while (0)
-
-    const int n_chunks = (T_n + SCAN_CT - 1) / SCAN_CT;
-    GDN_SCAN_FETCH(0);
+    const int n_chunks = (T_n + CT - 1) / CT;
+    GDN_CHUNK_FETCH(0);
     for (int c = 0; c < n_chunks; ++c) {
-        __syncthreads();  // previous chunk fully consumed
-        if (c > 0) GDN_SCAN_FLUSH(c - 1);
-        // registers -> LDS, plus k.q of each token (32 lanes per token)
-        *reinterpret_cast<float4 *>(&sk[tokA][colK]) = rkA;
-        *reinterpret_cast<float4 *>(&sq[tokA][colK]) = rqA;
-        *reinterpret_cast<float4 *>(&sk[tokB][colK]) = rkB;
-        *reinterpret_cast<float4 *>(&sq[tokB][colK]) = rqB;
-        float kqA = rkA.x * rqA.x, kqB = rkB.x * rqB.x;
-        kqA = fmaf(rkA.y, rqA.y, kqA);
-        kqB = fmaf(rkB.y, rqB.y, kqB);
-        kqA = fmaf(rkA.z, rqA.z, kqA);
-        kqB = fmaf(rkB.z, rqB.z, kqB);
-        kqA = fmaf(rkA.w, rqA.w, kqA);
-        kqB = fmaf(rkB.w, rqB.w, kqB);
-#pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) {
-            kqA += __shfl_xor(kqA, m, 32);
-            kqB += __shfl_xor(kqB, m, 32);
+        __syncthreads();  // the previous chunk is fully consumed
+        *reinterpret_cast<f4 *>(&sK[tA][colK]) = rkA;
+        *reinterpret_cast<f4 *>(&sQ[tA][colK]) = rqA;
+        *reinterpret_cast<f4 *>(&sK[tB][colK]) = rkB;
+        *reinterpret_cast<f4 *>(&sQ[tB][colK]) = rqB;
+        if (tid < 128) {
+            sVT[chV + 0][tV] = rv[0];
+            sVT[chV + 1][tV] = rv[1];
+            sVT[chV + 2][tV] = rv[2];
+            sVT[chV + 3][tV] = rv[3];
         }
-        if ((tid & 31) == 0) {
-            spar[tokA][2] = kqA;
-            spar[tokB][2] = kqB;
-        }
-        if (tid < 64) *reinterpret_cast<float4 *>(&sv[tokV][colV]) = rv;
-        if (tid < SCAN_CT) {
-            spar[tid][0] = expf(rg);
-            spar[tid][1] = rbeta;
-        }
-        if (c + 1 < n_chunks) GDN_SCAN_FETCH(c + 1);
+        if (tid >= SLOT_T0) *reinterpret_cast<f4 *>(&sP[4 * (tid - SLOT_T0)]) = rp;
+        if (c + 1 < n_chunks) GDN_CHUNK_FETCH(c + 1);
         __syncthreads();
 
-        const int nv = min(SCAN_CT, T_n - c * SCAN_CT);
+        const int nv = min(CT, T_n - c * CT);
+        const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
+
+        // partial P^T = K S0^T and R^T = Q S0^T over this wave's 64 keys
+        f4 P = z4, R = z4;
 #pragma unroll
-        for (int i = 0; i < SCAN_CT; ++i) {
-            if (i < nv) {  // uniform across the block
-                const float4 k0 = *reinterpret_cast<const float4 *>(&sk[i][j0]);
-                const float4 k1 = *reinterpret_cast<const float4 *>(&sk[i][j0 + 4]);
-                const float4 q0 = *reinterpret_cast<const float4 *>(&sq[i][j0]);
-                const float4 q1 = *reinterpret_cast<const float4 *>(&sq[i][j0 + 4]);
-                const float4 par = *reinterpret_cast<const float4 *>(&spar[i][0]);
-                const float v = sv[i][rl];
-                const float k[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-                const float q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-                float pk = S[0] * k[0], pq = S[0] * q[0];
+        for (int b = 0; b < 4; ++b) {
+            const int col = 16 * (4 * jh + b) + 4 * kk;
+            const f4 ka = *reinterpret_cast<const f4 *>(&sK[l16][col]);
+            const f4 qa = *reinterpret_cast<const f4 *>(&sQ[l16][col]);
 #pragma unroll
-                for (int e = 1; e < 8; ++e) {
-                    pk = fmaf(S[e], k[e], pk);
-                    pq = fmaf(S[e], q[e], pq);
-                }
-                pk = row_sum16(pk);
-                pq = row_sum16(pq);
-                const float alpha = par.x, beta = par.y, kq = par.z;
-                const float uu = beta * (v - alpha * pk);
-                const float out = (alpha * pq + uu * kq) * scale;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) S[e] = fmaf(uu, k[e], alpha * S[e]);
-                if (l16 == 0) so[i][rl] = out;
+            for (int r = 0; r < 4; ++r) {
+                P = mfma4(ka[r], S4[b][r], P);
+                R = mfma4(qa[r], S4[b][r], R);
             }
         }
+        *reinterpret_cast<f4 *>(&sX[wave][0][lane][0]) = P;
+        *reinterpret_cast<f4 *>(&sX[wave][1][lane][0]) = R;
+        __syncthreads();
+        {
+            const int w0 = wave & ~1;  // key half 0 first, in both waves of the pair
+            P = *reinterpret_cast<const f4 *>(&sX[w0][0][lane][0]) +
+                *reinterpret_cast<const f4 *>(&sX[w0 + 1][0][lane][0]);
+            R = *reinterpret_cast<const f4 *>(&sX[w0][1][lane][0]) +
+                *reinterpret_cast<const f4 *>(&sX[w0 + 1][1][lane][0]);
+        }
+        // B = beta (V - Lam P), component r is token 4 kk + r, channel l16
+        const f4 lam = *reinterpret_cast<const f4 *>(&sP[OFF_LAM + 4 * kk]);
+        const f4 bet = *reinterpret_cast<const f4 *>(&sP[OFF_BETA + 4 * kk]);
+        const f4 vv = *reinterpret_cast<const f4 *>(&sVT[rs * 16 + l16][4 * kk]);
+        f4 Bm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Bm[r] = bet[r] * (vv[r] - lam[r] * P[r]);
+        // U = T B
+        const f4 trow = *reinterpret_cast<const f4 *>(&sP[OFF_T + l16 * CT + 4 * kk]);
+        f4 U = z4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U = mfma4(trow[r], Bm[r], U);
+
+        if (jh == 0) {
+            // O = Lam R + M U (both pre-scaled by 1/sqrt(dk))
+            const f4 lams = *reinterpret_cast<const f4 *>(&sP[OFF_LAMS + 4 * kk]);
+            const f4 mrow = *reinterpret_cast<const f4 *>(&sP[OFF_M + l16 * CT + 4 * kk]);
+            f4 O;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[r] = lams[r] * R[r];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O = mfma4(mrow[r], U[r], O);
+            float *orow = p.o + (tb * hv + h) * 128 + rb * 32 + rs * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kk + r;
+                if (t < nv) orow[(int64_t)t * hv * 128] = O[r];
+            }
+        }
+
+        // S' = Lam_last S0 + (D[last] K)^T U on this wave's 64 keys
+        const float last = sP[OFF_LAST];
+        const f4 wv = *reinterpret_cast<const f4 *>(&sP[OFF_W + 4 * kk]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int col = 16 * (4 * jh + b) + l16;
+            f4 C = S4[b] * last;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) C = mfma4(wv[r] * sK[4 * kk + r][col], U[r], C);
+            S4[b] = C;
+        }
     }
-    __syncthreads();
-    GDN_SCAN_FLUSH(n_chunks - 1);
-#undef GDN_SCAN_FETCH
-#undef GDN_SCAN_FLUSH
-    store8(Sp, S);
+#undef GDN_CHUNK_FETCH
+#pragma unroll
+    for (int b = 0; b < 4; ++b) *reinterpret_cast<f4 *>(Srow + 16 * b) = S4[b];
 }
 
 hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
 {
-    ScanDims d;
-    d.hk = s.hk;
-    d.hv = s.hv;
-    d.G = s.hv / s.hk;
-    d.blocks_per_head = 128 / SCAN_RB;
-    const int64_t blocks = (int64_t)s.n_seq * s.hv * d.blocks_per_head;
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, d);
+    PrepDims pd;
+    pd.hk = s.hk;
+    pd.hv = s.hv;
+    pd.G = s.hv / s.hk;
+    pd.n_chunk_max = (int)((s.max_T + CT - 1) / CT);
+    hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk),
+                       dim3(256), 0, st, a, pd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ChunkDims cd;
+    cd.hk = s.hk;
+    cd.hv = s.hv;
+    cd.G = s.hv / s.hk;
+    const int64_t blocks = (int64_t)s.n_seq * s.hv * 4;
+    hipLaunchKernelGGL(scan_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, cd);
     return hipGetLastError();
+}
+
+size_t scan_workspace_bytes(const gdn_shape &s)
+{
+    const size_t slots = (size_t)(s.total_T / CT) + (size_t)s.n_seq + 1;
+    return slots * (size_t)s.hv * SCAN_SLOT_FLOATS * sizeof(float);
 }
 
 } // namespace gdn

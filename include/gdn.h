@@ -53,8 +53,8 @@
  *   z       [total_T][hv][dv] io   output-gate input
  *   gamma   [dv]              io   RMSNorm weight shared by all value heads
  *   y       [total_T][hv][dv] shape->out_dtype
- * Alignment: qkv, conv_w, hist, qn, kn, vc, state, o, z, gamma, y and the
- * workspace must be 16-byte aligned; a, b, A_log, dt_bias, g, beta and
+ * Alignment: workspaces 256-byte; qkv, conv_w, hist, qn, kn, vc, state, o,
+ * z, gamma and y 16-byte; a, b, A_log, dt_bias, g, beta and
  * cu_seqlens 4-byte aligned (GDN_E_ALIGN otherwise).
  * No two buffers may overlap, except where an argument is documented as
  * read-then-overwritten in place (hist, state).
@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -143,14 +143,25 @@ int gdn_pre(const gdn_shape *shape, const int32_t *cu_seqlens,
  *   alpha = exp(g[t][h])
  *   S <- alpha*S + beta[t][h] * (vc[t][h] - alpha*S kn[t][j]) kn[t][j]^T
  *   o[t][h] = S qn[t][j] / sqrt(dk)
+ * The kernels evaluate this exactly (up to fp32 rounding) in 16-token chunks
+ * counted from each sequence's first token.  Splitting a sequence across calls
+ * at a multiple of 16 tokens is therefore bit-identical to one call; any other
+ * split agrees within fp32 rounding.
  * In:  cu_seqlens, qn, kn, vc, g, beta; state (read: S at the start).
  * Out: o; state (overwritten in place with S after the last token).
- * The result is bitwise independent of how a sequence is split across calls.
+ * workspace: device scratch of >= gdn_scan_workspace_bytes(shape) bytes,
+ * 256-byte aligned, owned by the caller; its contents are undefined after the
+ * call and it must not be shared by calls in flight at the same time.
  */
 int gdn_scan(const gdn_shape *shape, const int32_t *cu_seqlens,
              const float *qn, const float *kn, const float *vc,
              const float *g, const float *beta, float *state, float *o,
-             void *stream);
+             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of scratch gdn_scan needs for `shape` (0 if the shape is invalid):
+ * one 2560-byte slot per (16-token chunk, value head), at most
+ * (total_T/16 + n_seq + 1) * hv slots. */
+size_t gdn_scan_workspace_bytes(const gdn_shape *shape);
 
 /*
  * gdn_post -- "Round 30 Track C Audit", section 1 (gdn_post): one sum of
@@ -166,15 +177,17 @@ int gdn_post(const gdn_shape *shape, const float *o, const void *z,
              const void *gamma, void *y, void *stream);
 
 /* Bytes of workspace gdn_prefill_layer needs for `shape` (0 if the shape is
- * invalid): room for qn, kn, vc, g, beta and o, each 256-byte aligned. */
+ * invalid): room for qn, kn, vc, g, beta, o and the scan scratch, each
+ * 256-byte aligned. */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
 
 /*
  * gdn_prefill_layer -- the three stages above in order on one stream, the
  * whole path of one layer.  Arguments are those of gdn_pre, gdn_scan and
- * gdn_post; the fp32 intermediates live in `workspace`
- * (>= gdn_prefill_workspace_bytes(shape) bytes, device memory, contents
- * undefined afterwards).  hist and state are read and overwritten in place.
+ * gdn_post; the fp32 intermediates and the scan scratch live in `workspace`
+ * (>= gdn_prefill_workspace_bytes(shape) bytes, device memory, 256-byte
+ * aligned, contents undefined afterwards, not shared by calls in flight at the
+ * same time).  hist and state are read and overwritten in place.
  */
 int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens,
                       const void *qkv, const void *conv_w, const void *a,

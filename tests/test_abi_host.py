@@ -25,13 +25,14 @@ def shape(**kw):
 def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_pre", "gdn_scan",
-                          "gdn_post", "gdn_prefill_workspace_bytes", "gdn_prefill_layer"}
+                          "gdn_scan_workspace_bytes", "gdn_post", "gdn_prefill_workspace_bytes",
+                          "gdn_prefill_layer"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert B.gdn_abi_version() == 1
+    assert B.gdn_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.gdn_status_str(code) and B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(-99) == "unknown status"
@@ -46,9 +47,15 @@ def test_workspace_bytes():
     s = shape(total_T=2048, max_T=2048)
     T = 2048
     r = lambda x: (x + 255) // 256 * 256
-    want = 2 * r(T * 16 * 128 * 4) + r(T * 48 * 128 * 4) * 2 + 2 * r(T * 48 * 4)
+    scan = (T // 16 + 1 + 1) * 48 * 640 * 4    # one 640-float slot per (chunk, value head)
+    assert B.gdn_scan_workspace_bytes(s) == scan
+    want = 2 * r(T * 16 * 128 * 4) + r(T * 48 * 128 * 4) * 2 + 2 * r(T * 48 * 4) + r(scan)
     assert B.gdn_prefill_workspace_bytes(s) == want
     assert B.gdn_prefill_workspace_bytes(shape(hv=47)) == 0
+    assert B.gdn_scan_workspace_bytes(shape(hv=47)) == 0
+    # varlen: at most total_T / 16 + n_seq slots per value head
+    v = shape(n_seq=4, total_T=27135, max_T=16384)
+    assert B.gdn_scan_workspace_bytes(v) == (27135 // 16 + 4 + 1) * 48 * 640 * 4
 
 
 def _pre(s, **over):
@@ -60,10 +67,10 @@ def _pre(s, **over):
                      args["vc"], args["g"], args["beta"], stream=0, check=False)
 
 
-def _scan(s, **over):
-    args = dict(cu=P, qn=P, kn=P, vc=P, g=P, beta=P, state=P, o=P)
+def _scan(s, ws_bytes=1 << 40, **over):
+    args = dict(cu=P, qn=P, kn=P, vc=P, g=P, beta=P, state=P, o=P, ws=P)
     args.update(over)
-    return B.gdn_scan(s, *args.values(), stream=0, check=False)
+    return B.gdn_scan(s, *args.values(), workspace_bytes=ws_bytes, stream=0, check=False)
 
 
 def _post(s, **over):
@@ -101,7 +108,7 @@ def test_bad_shapes_rejected_by_every_entry_point(over, code):
 
 
 def test_null_shape_pointer(L):
-    assert L.gdn_scan(None, *([P] * 8), None) == -1
+    assert L.gdn_scan(None, *([P] * 9), 1 << 30, None) == -1
     assert L.gdn_prefill_workspace_bytes(None) == 0
 
 
@@ -118,10 +125,17 @@ def test_pre_alignment(name, off, code):
     assert _pre(shape(), **{name: P + off}) == code
 
 
-@pytest.mark.parametrize("name", ["cu", "qn", "kn", "vc", "g", "beta", "state", "o"])
+@pytest.mark.parametrize("name", ["cu", "qn", "kn", "vc", "g", "beta", "state", "o", "ws"])
 def test_scan_null_and_alignment(name):
     assert _scan(shape(), **{name: None}) == -1
     assert _scan(shape(), **{name: P + 2}) == -3
+
+
+def test_scan_workspace_size_and_alignment():
+    s = shape()
+    need = B.gdn_scan_workspace_bytes(s)
+    assert _scan(s, ws_bytes=need - 1) == -4
+    assert _scan(s, ws=P + 128) == -3     # scratch needs 256-byte alignment
 
 
 @pytest.mark.parametrize("name", ["o", "z", "gamma", "y"])
@@ -144,6 +158,6 @@ def test_zero_tokens_is_a_noop_that_succeeds():
     s = shape(total_T=0, max_T=0, n_seq=3)
     # nothing is validated beyond the shape and nothing is launched
     assert _pre(s, qkv=None) == 0
-    assert _scan(s, o=None) == 0
+    assert _scan(s, o=None, ws=None, ws_bytes=0) == 0
     assert _post(s, y=None) == 0
     assert _layer(s, ws=None, ws_bytes=0) == 0

@@ -15,6 +15,7 @@ import torch
 
 from gated_deltanet_linear_pre_amd import binding as B
 from gated_deltanet_linear_pre_amd import synth
+from gated_deltanet_linear_pre_amd import buffers
 from gated_deltanet_linear_pre_amd.buffers import upload
 from oracle import gdn_oracle as orc
 
@@ -24,6 +25,10 @@ from .gpu_util import Guarded, banner, np_
 pytestmark = pytest.mark.gpu
 
 F32 = torch.float32
+
+
+def scratch(s):
+    return buffers.scratch(B.gdn_scan_workspace_bytes(s), "cuda")
 
 
 def _cu(lens):
@@ -91,11 +96,13 @@ def test_scan_matches_oracle(gpu, case):
     state = Guarded(d["S0"].shape, F32, init=torch.from_numpy(d["S0"]))
     o = Guarded((T, hv, 128), F32)
     s = B.make_shape(hk, hv, n, T, max(lens), io="f32", out="f32")
+    ws = Guarded((B.gdn_scan_workspace_bytes(s) // 4,), F32)
     banner("gdn_scan", name, f"T={T}", f"lens={lens}")
     B.gdn_scan(s, upload(cu, dev), upload(d["qn"], dev), upload(d["kn"], dev),
-               upload(d["vc"], dev), upload(d["g"], dev), upload(d["beta"], dev), state.t, o.t)
+               upload(d["vc"], dev), upload(d["g"], dev), upload(d["beta"], dev), state.t, o.t,
+               ws.t)
     torch.cuda.synchronize()
-    assert state.intact() and o.intact()
+    assert state.intact() and o.intact() and ws.intact()
     parity.check_o(np_(o.t), o_ref)
     parity.check_state(np_(state.t), S_ref)
     # sequences of length 0 keep their state bit for bit
@@ -112,10 +119,11 @@ def test_scan_invariant_beta0_g0_keeps_state_bitwise(gpu):
     dev = "cuda"
     state = upload(d["S0"], dev)
     o = torch.empty((T, hv, 128), dtype=F32, device=dev)
+    s = B.make_shape(hk, hv, 1, T, T, io="f32", out="f32")
     banner("gdn_scan", "beta=0,g=0")
-    B.gdn_scan(B.make_shape(hk, hv, 1, T, T, io="f32", out="f32"), upload(_cu([T]), dev),
+    B.gdn_scan(s, upload(_cu([T]), dev),
                upload(d["qn"], dev), upload(d["kn"], dev), upload(d["vc"], dev),
-               upload(d["g"], dev), upload(d["beta"], dev), state, o)
+               upload(d["g"], dev), upload(d["beta"], dev), state, o, scratch(s))
     torch.cuda.synchronize()
     assert np.array_equal(np_(state), d["S0"])
     # o_t = S0 q_t / sqrt(dk): compare with the oracle's scan of the same inputs
@@ -140,11 +148,12 @@ def test_scan_invariant_unit_key_writes_value(gpu):
     for t_end in (1, 7, 24):
         state = upload(d["S0"], dev)
         o = torch.empty((t_end, hv, 128), dtype=F32, device=dev)
+        s = B.make_shape(hk, hv, 1, t_end, t_end, io="f32", out="f32")
         banner("gdn_scan", "unit-key", f"T={t_end}")
-        B.gdn_scan(B.make_shape(hk, hv, 1, t_end, t_end, io="f32", out="f32"),
-                   upload(_cu([t_end]), dev), upload(d["qn"][:t_end], dev),
+        B.gdn_scan(s, upload(_cu([t_end]), dev), upload(d["qn"][:t_end], dev),
                    upload(d["kn"][:t_end], dev), upload(d["vc"][:t_end], dev),
-                   upload(d["g"][:t_end], dev), upload(d["beta"][:t_end], dev), state, o)
+                   upload(d["g"][:t_end], dev), upload(d["beta"][:t_end], dev), state, o,
+                   scratch(s))
         torch.cuda.synchronize()
         S = np_(state)[0]
         col = S[:, :, js[t_end - 1]]
