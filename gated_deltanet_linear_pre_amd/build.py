@@ -25,6 +25,8 @@ CFLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # keep the compiler from forming packed-fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around the chains)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(HERE, "..", "include"),
 ]
 

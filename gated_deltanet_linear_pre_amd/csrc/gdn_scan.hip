@@ -48,6 +48,8 @@
 // channel block add the key halves in the same order, so they agree bit for
 // bit.  Splitting a sequence at a multiple of 16 tokens gives bit-identical
 // results; other split points agree within rounding (the chunk grid moves).
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -205,16 +207,28 @@ struct ChunkDims {
     int hk, hv, G;
 };
 
+// LDS strides (floats): rows padded so 16 lanes reading 16 rows hit distinct
+// banks as far as a 16-byte read allows.
+constexpr int TS_ = 20;   // T, M and V^T rows
+constexpr int VEC = 80;   // Lam, Lam/sqrt(dk), beta, D[last][.], Lam_last
+
 __global__ __launch_bounds__(256) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
 {
-    __shared__ __attribute__((aligned(16))) float sK[CT][KS];
-    __shared__ __attribute__((aligned(16))) float sQ[CT][KS];
-    __shared__ __attribute__((aligned(16))) float sVT[32][20];  // v, [channel][token]
-    __shared__ __attribute__((aligned(16))) float sP[SCAN_SLOT_FLOATS];
-    __shared__ __attribute__((aligned(16))) float sX[4][2][64][4];  // partial P, R
+    // Staging buffers, indexed by chunk: K, V and the prep data are read after
+    // the chunk's one barrier, so they rotate through 3 buffers; Q is read
+    // only before it, so 2 suffice.  The partial sums rotate through 2.
+    __shared__ __attribute__((aligned(16))) float sK[3][CT][KS];
+    __shared__ __attribute__((aligned(16))) float sQ[2][CT][KS];
+    __shared__ __attribute__((aligned(16))) float sV[3][32][TS_];   // v, [channel][token]
+    __shared__ __attribute__((aligned(16))) float sT[3][CT][TS_];
+    __shared__ __attribute__((aligned(16))) float sM[3][CT][TS_];
+    __shared__ __attribute__((aligned(16))) float sVec[3][VEC];
+    __shared__ __attribute__((aligned(16))) float sX[2][4][2][64][4];  // partial P, R
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
+    // wave index as a scalar: everything derived from it stays in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
 
     // XCD-aware work index -> (sequence n, value head h, 32-channel block rb)
     const int nb = gridDim.x;
@@ -242,129 +256,175 @@ __global__ __launch_bounds__(256) void scan_chunk_kernel(ScanArgs p, ChunkDims d
 #pragma unroll
     for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b);
 
-    // staging roles (next chunk prefetched into registers): k and q rows by
-    // all 256 threads, v by threads 0..127, the prep slot (160 float4) by
-    // threads 96..255
-    constexpr int SLOT_T0 = 256 - SCAN_SLOT_FLOATS / 4;
-    static_assert(SLOT_T0 >= 0, "prep slot larger than one float4 per thread");
+    // Staging roles: k and q rows by all 256 threads (2 float4 each), v by
+    // threads 0..127, the prep slot (T, M: 128 float4; the vectors: 20) by
+    // threads 96..243.
+    constexpr int SLOT_T0 = 96;
     const int tA = tid >> 5, tB = tA + 8, colK = (tid & 31) * 4;
     const int tV = tid >> 3, chV = (tid & 7) * 4;  // tid < 128
+    const int fP = tid - SLOT_T0;                  // prep float4 index, 0..147
     f4 rkA = z4, rkB = z4, rqA = z4, rqB = z4, rv = z4, rp = z4;
-
-#define GDN_CHUNK_FETCH(c_)                                                            \
-    do {                                                                               \
-        const int64_t tb_ = (int64_t)cu0 + (int64_t)(c_) * CT;                         \
-        const int nv_ = min(CT, T_n - (c_) * CT);                                      \
-        const int64_t ks_ = (int64_t)hk * 128;                                         \
-        const float *kb_ = p.kn + (tb_ * hk + j) * 128 + colK;                         \
-        const float *qb_ = p.qn + (tb_ * hk + j) * 128 + colK;                         \
-        const int ta_ = min(tA, nv_ - 1), tb2_ = min(tB, nv_ - 1);                     \
-        const f4 k0_ = *reinterpret_cast<const f4 *>(kb_ + ta_ * ks_);                 \
-        const f4 q0_ = *reinterpret_cast<const f4 *>(qb_ + ta_ * ks_);                 \
-        const f4 k1_ = *reinterpret_cast<const f4 *>(kb_ + tb2_ * ks_);                \
-        const f4 q1_ = *reinterpret_cast<const f4 *>(qb_ + tb2_ * ks_);                \
-        rkA = tA < nv_ ? k0_ : z4;                                                     \
-        rqA = tA < nv_ ? q0_ : z4;                                                     \
-        rkB = tB < nv_ ? k1_ : z4;                                                     \
-        rqB = tB < nv_ ? q1_ : z4;                                                     \
-        if (tid < 128) {                                                               \
-            const f4 v_ = *reinterpret_cast<const f4 *>(                               \
-                p.vc + ((tb_ + min(tV, nv_ - 1)) * hv + h) * 128 + rb * 32 + chV);     \
-            rv = tV < nv_ ? v_ : z4;                                                   \
-        }                                                                              \
-        if (tid >= SLOT_T0)                                                            \
-            rp = *reinterpret_cast<const f4 *>(                                        \
-                p.ws + (chunk_slot(cu0, n, (c_)) * hv + h) * SCAN_SLOT_FLOATS +         \
-                4 * (tid - SLOT_T0));                                                  \
-    } while (0)
-
     const int n_chunks = (T_n + CT - 1) / CT;
-    GDN_CHUNK_FETCH(0);
-    for (int c = 0; c < n_chunks; ++c) {
-        __syncthreads();  // the previous chunk is fully consumed
-        *reinterpret_cast<f4 *>(&sK[tA][colK]) = rkA;
-        *reinterpret_cast<f4 *>(&sQ[tA][colK]) = rqA;
-        *reinterpret_cast<f4 *>(&sK[tB][colK]) = rkB;
-        *reinterpret_cast<f4 *>(&sQ[tB][colK]) = rqB;
-        if (tid < 128) {
-            sVT[chV + 0][tV] = rv[0];
-            sVT[chV + 1][tV] = rv[1];
-            sVT[chV + 2][tV] = rv[2];
-            sVT[chV + 3][tV] = rv[3];
-        }
-        if (tid >= SLOT_T0) *reinterpret_cast<f4 *>(&sP[4 * (tid - SLOT_T0)]) = rp;
-        if (c + 1 < n_chunks) GDN_CHUNK_FETCH(c + 1);
-        __syncthreads();
+    const uint32_t kstride = (uint32_t)hk * 128;   // floats per token row of qn/kn
+    const uint32_t vstride = (uint32_t)hv * 128;
 
+    // Global loads only.  Rows past the sequence's end are read from its last
+    // token instead (always valid memory) and then carry no weight: the prep
+    // slot gives them beta = Lam = 0 and zero decay weights, and T is the
+    // identity there, so they add exactly nothing to U, O or the state.
+    // Addresses are a uniform base (SGPRs) plus a 32-bit byte offset per lane,
+    // the form the global loads take directly.
+    auto ld4 = [](const float *base, uint32_t byte_off) {
+        return *reinterpret_cast<const f4 *>(reinterpret_cast<const char *>(base) + byte_off);
+    };
+    auto fetch = [&](int c) {
+        const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
+        const int nv = min(CT, T_n - c * CT);
+        const float *kc = p.kn + (tb * hk + j) * 128;
+        const float *qc = p.qn + (tb * hk + j) * 128;
+        const uint32_t oA = ((uint32_t)min(tA, nv - 1) * kstride + colK) * 4u;
+        const uint32_t oB = ((uint32_t)min(tB, nv - 1) * kstride + colK) * 4u;
+        rkA = ld4(kc, oA);
+        rqA = ld4(qc, oA);
+        rkB = ld4(kc, oB);
+        rqB = ld4(qc, oB);
+        if (tid < 128)
+            rv = ld4(p.vc + (tb * hv + h) * 128 + rb * 32,
+                     ((uint32_t)min(tV, nv - 1) * vstride + chV) * 4u);
+        if (fP >= 0 && fP < 148)
+            rp = ld4(p.ws + (chunk_slot(cu0, n, c) * hv + h) * SCAN_SLOT_FLOATS, 16u * fP);
+    };
+    // registers -> the LDS buffers (b3, b2) of the chunk they hold
+    auto stage = [&](auto b3c, auto b2c) {
+        constexpr int b3 = decltype(b3c)::value, b2 = decltype(b2c)::value;
+        *reinterpret_cast<f4 *>(&sK[b3][tA][colK]) = rkA;
+        *reinterpret_cast<f4 *>(&sK[b3][tB][colK]) = rkB;
+        *reinterpret_cast<f4 *>(&sQ[b2][tA][colK]) = rqA;
+        *reinterpret_cast<f4 *>(&sQ[b2][tB][colK]) = rqB;
+        if (tid < 128) {
+            sV[b3][chV + 0][tV] = rv[0];
+            sV[b3][chV + 1][tV] = rv[1];
+            sV[b3][chV + 2][tV] = rv[2];
+            sV[b3][chV + 3][tV] = rv[3];
+        }
+        if (fP >= 0 && fP < 64)
+            *reinterpret_cast<f4 *>(&sT[b3][fP >> 2][(fP & 3) * 4]) = rp;
+        else if (fP >= 64 && fP < 128)
+            *reinterpret_cast<f4 *>(&sM[b3][(fP - 64) >> 2][(fP & 3) * 4]) = rp;
+        else if (fP >= 128 && fP < 148)
+            *reinterpret_cast<f4 *>(&sVec[b3][4 * (fP - 128)]) = rp;
+    };
+
+    // One chunk, with its LDS buffers (b3, b2) known at compile time.
+    auto step = [&](auto b3c, auto b2c, int c) {
+        constexpr int b3 = decltype(b3c)::value, b2 = decltype(b2c)::value;
         const int nv = min(CT, T_n - c * CT);
         const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
+        // next chunk to LDS (its buffers were last read two chunks ago, before
+        // the previous barrier), then start loading the one after
+        if (c + 1 < n_chunks) {
+            stage(std::integral_constant<int, (b3 + 1) % 3>{}, std::integral_constant<int, b2 ^ 1>{});
+            if (c + 2 < n_chunks) fetch(c + 2);
+        }
+
+        // Every LDS operand of this chunk except the partner's partial sums is
+        // in place already: read them all before the barrier, so that after it
+        // only the exchange waits on LDS.
+        f4 ka[4], qa[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int col = 16 * (4 * jh + b) + 4 * kk;
+            ka[b] = *reinterpret_cast<const f4 *>(&sK[b3][l16][col]);
+            qa[b] = *reinterpret_cast<const f4 *>(&sQ[b2][l16][col]);
+        }
+        const float *vec = sVec[b3];
+        const f4 lam = *reinterpret_cast<const f4 *>(vec + 4 * kk);
+        const f4 lams = *reinterpret_cast<const f4 *>(vec + 16 + 4 * kk);
+        const f4 bet = *reinterpret_cast<const f4 *>(vec + 32 + 4 * kk);
+        const f4 wv = *reinterpret_cast<const f4 *>(vec + 48 + 4 * kk);
+        const float last = vec[64];
+        const f4 vv = *reinterpret_cast<const f4 *>(&sV[b3][rs * 16 + l16][4 * kk]);
+        const f4 trow = *reinterpret_cast<const f4 *>(&sT[b3][l16][4 * kk]);
+        const f4 mrow = *reinterpret_cast<const f4 *>(&sM[b3][l16][4 * kk]);
+        // A operand of the state update, K^T: key 16 (4 jh + b) + l16, token 4 kk + r
+        float ak[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) ak[r][b] = sK[b3][4 * kk + r][16 * (4 * jh + b) + l16];
+        }
 
         // partial P^T = K S0^T and R^T = Q S0^T over this wave's 64 keys
         f4 P = z4, R = z4;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int col = 16 * (4 * jh + b) + 4 * kk;
-            const f4 ka = *reinterpret_cast<const f4 *>(&sK[l16][col]);
-            const f4 qa = *reinterpret_cast<const f4 *>(&sQ[l16][col]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                P = mfma4(ka[r], S4[b][r], P);
-                R = mfma4(qa[r], S4[b][r], R);
+                P = mfma4(ka[b][r], S4[b][r], P);
+                R = mfma4(qa[b][r], S4[b][r], R);
             }
         }
-        *reinterpret_cast<f4 *>(&sX[wave][0][lane][0]) = P;
-        *reinterpret_cast<f4 *>(&sX[wave][1][lane][0]) = R;
-        __syncthreads();
+        f4 C[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) C[b] = S4[b] * last;
+        *reinterpret_cast<f4 *>(&sX[b2][wave][0][lane][0]) = P;
+        *reinterpret_cast<f4 *>(&sX[b2][wave][1][lane][0]) = R;
+        __syncthreads();  // the one barrier per chunk
         {
-            const int w0 = wave & ~1;  // key half 0 first, in both waves of the pair
-            P = *reinterpret_cast<const f4 *>(&sX[w0][0][lane][0]) +
-                *reinterpret_cast<const f4 *>(&sX[w0 + 1][0][lane][0]);
-            R = *reinterpret_cast<const f4 *>(&sX[w0][1][lane][0]) +
-                *reinterpret_cast<const f4 *>(&sX[w0 + 1][1][lane][0]);
+            // both waves of the pair add key half 0 + key half 1 (same bits)
+            const f4 Po = *reinterpret_cast<const f4 *>(&sX[b2][wave ^ 1][0][lane][0]);
+            const f4 Ro = *reinterpret_cast<const f4 *>(&sX[b2][wave ^ 1][1][lane][0]);
+            P = jh == 0 ? P + Po : Po + P;
+            R = jh == 0 ? R + Ro : Ro + R;
         }
         // B = beta (V - Lam P), component r is token 4 kk + r, channel l16
-        const f4 lam = *reinterpret_cast<const f4 *>(&sP[OFF_LAM + 4 * kk]);
-        const f4 bet = *reinterpret_cast<const f4 *>(&sP[OFF_BETA + 4 * kk]);
-        const f4 vv = *reinterpret_cast<const f4 *>(&sVT[rs * 16 + l16][4 * kk]);
         f4 Bm;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Bm[r] = bet[r] * (vv[r] - lam[r] * P[r]);
         // U = T B
-        const f4 trow = *reinterpret_cast<const f4 *>(&sP[OFF_T + l16 * CT + 4 * kk]);
         f4 U = z4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) U = mfma4(trow[r], Bm[r], U);
-
+        // S' = Lam_last S0 + K^T (D[last] U) on this wave's 64 keys
+        const f4 Uw = U * wv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) C[b] = mfma4(ak[r][b], Uw[r], C[b]);
+        }
         if (jh == 0) {
             // O = Lam R + M U (both pre-scaled by 1/sqrt(dk))
-            const f4 lams = *reinterpret_cast<const f4 *>(&sP[OFF_LAMS + 4 * kk]);
-            const f4 mrow = *reinterpret_cast<const f4 *>(&sP[OFF_M + l16 * CT + 4 * kk]);
-            f4 O;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[r] = lams[r] * R[r];
+            f4 O = lams * R;
 #pragma unroll
             for (int r = 0; r < 4; ++r) O = mfma4(mrow[r], U[r], O);
-            float *orow = p.o + (tb * hv + h) * 128 + rb * 32 + rs * 16 + l16;
+            char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * 32 + rs * 16);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * kk + r;
-                if (t < nv) orow[(int64_t)t * hv * 128] = O[r];
+                if (t < nv)
+                    *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r];
             }
         }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) S4[b] = C[b];
+    };
 
-        // S' = Lam_last S0 + (D[last] K)^T U on this wave's 64 keys
-        const float last = sP[OFF_LAST];
-        const f4 wv = *reinterpret_cast<const f4 *>(&sP[OFF_W + 4 * kk]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int col = 16 * (4 * jh + b) + l16;
-            f4 C = S4[b] * last;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) C = mfma4(wv[r] * sK[4 * kk + r][col], U[r], C);
-            S4[b] = C;
-        }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    fetch(0);
+    stage(I0{}, I0{});
+    if (n_chunks > 1) fetch(1);
+    __syncthreads();
+    // unrolled by 6 = lcm(3, 2) so every buffer index is a constant
+    for (int c = 0; c < n_chunks; c += 6) {
+        step(I0{}, I0{}, c);
+        if (c + 1 < n_chunks) step(I1{}, I1{}, c + 1);
+        if (c + 2 < n_chunks) step(I2{}, I0{}, c + 2);
+        if (c + 3 < n_chunks) step(I0{}, I1{}, c + 3);
+        if (c + 4 < n_chunks) step(I1{}, I0{}, c + 4);
+        if (c + 5 < n_chunks) step(I2{}, I1{}, c + 5);
     }
-#undef GDN_CHUNK_FETCH
 #pragma unroll
     for (int b = 0; b < 4; ++b) *reinterpret_cast<f4 *>(Srow + 16 * b) = S4[b];
 }
