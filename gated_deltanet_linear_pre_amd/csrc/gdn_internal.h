@@ -23,8 +23,11 @@ struct ScanArgs {
     float *ws;  // per-(chunk, value head) prep slots
 };
 
-// floats per (16-token chunk, value head) slot of the scan workspace
-constexpr int SCAN_SLOT_FLOATS = 640;
+// Scan workspace: per 16-token chunk, one key-head slot per key head (K, Q
+// and K^T as split fp16 MFMA operands, 24 KB) and one value-head slot per
+// value head (T, M as split fp16 operands plus the chunk's decay vectors).
+constexpr int SCAN_KH_FLOATS = 6144;
+constexpr int SCAN_SLOT_FLOATS = 576;
 size_t scan_workspace_bytes(const gdn_shape &s);
 
 struct PostArgs {

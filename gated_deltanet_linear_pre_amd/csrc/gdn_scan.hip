@@ -1,5 +1,5 @@
 // gdn_scan.hip -- the gated delta rule on an fp32 state, in 16-token chunks on
-// fp32 MFMA.
+// fp16 MFMA with split (hi + lo) operands.
 //
 // "Round 30 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 1
 // (gdn_scan_r findings): one state per value head, updated token by token in
@@ -9,45 +9,60 @@
 // The recurrence, per value head h (key head j = h / G), state S (dv x dk):
 //   S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) k_t^T,
 //   o_t = S_t q_t / sqrt(dk),  alpha_t = exp(g_t).
-// Over a chunk of C = 16 tokens starting from state S0, with
+// Over a chunk of 16 tokens starting from state S0, with
 //   D[t][s] = exp(g_{s+1} + ... + g_t)    (decay from just after s to t, <= 1)
 //   Lam_t   = exp(g_0 + ... + g_t)        (decay from the chunk start)
 // the writes u_t = beta_t (v_t - alpha_t S_{t-1} k_t) solve a unit lower
 // triangular system, and the outputs and the next state follow:
 //   (I + A) U = diag(beta) (V - diag(Lam) P),  A[t][s] = beta_t D[t][s] k_t.k_s (s<t)
-//   O  = diag(Lam) R + M U,                     M[t][s] = D[t][s] q_t.k_s     (s<=t)
+//   O  = (diag(Lam) R + M U) / sqrt(dk),       M[t][s] = D[t][s] q_t.k_s     (s<=t)
 //   S' = Lam_last S0 + sum_s D[last][s] u_s k_s^T
 // with P = K S0^T, R = Q S0^T (tokens x value channels).  This is exact
 // algebra of the recurrence (unroll S_t = Lam_t S0 + sum_{s<=t} D[t][s] u_s k_s^T).
 // Every decay is formed as exp of a sum of at most 16 log decays, never as a
 // ratio of two cumulative products, so nothing overflows or cancels.
 //
-// gfx950 mapping.
-// * gdn_scan_prep (fully parallel over sequence x chunk x key head): k.k and
-//   q.k of the chunk on MFMA (once per key head, shared by its G value heads),
-//   then per value head the decays, T = (I + A)^-1 by forward substitution (one
-//   column per lane, in registers), M, Lam, beta and the last-row decays.  The
-//   result goes to one slot per (chunk, value head) of the workspace.
-// * gdn_scan_chunk (sequential over chunks): a block of 4 waves owns 32 value
-//   channels of one (sequence, value head).  Each wave holds a 16-channel x
-//   64-key quarter of the state in MFMA accumulator layout (16 VGPRs/lane).
-//   Per chunk: K S0^T and Q S0^T over the wave's 64 keys (32 MFMA
-//   16x16x4 f32), the partial sums of the two key halves exchanged through
-//   LDS, U = T B (4 MFMA), O = Lam R + M U (4 MFMA, one wave per pair), and the
-//   state update Lam_last S0 + (D K)^T U (16 MFMA).  The state never leaves
-//   registers, and every product consumes the accumulator layout the previous
-//   one produced: the contraction index is permuted consistently, so no
-//   transposes are needed.
-//   The next chunk's K, Q, V and prep slot are loaded into registers while the
-//   current chunk computes.
-// * Block order is XCD-aware (blocks are dealt round-robin to the 8 XCDs; the
-//   index is permuted so each XCD gets whole heads and whole key-head groups,
-//   sharing their K/Q stream in one L2).
+// Precision.  Every product of the chunk step runs on fp16 MFMA with fp32
+// accumulation, each fp32 operand x split into hi = fp16(x) and
+// lo = fp16(x - hi): x*y ~ hi_x hi_y + hi_x lo_y + lo_x hi_y, good to about
+// 2^-21 relative per product (the dropped lo_x lo_y term and the rounding of
+// lo).  k, q and the state are scaled by 16 (exactly) so that the lo parts
+// stay out of fp16 subnormals; the state stays fp32 in the MFMA accumulators.
+// Operands must stay inside the fp16 range after scaling (|state| < 4e3,
+// |v|, |u| < 6.5e4); beyond it the result turns to inf/NaN, never silently
+// wrong.
 //
-// Determinism: fixed-order MFMA chains, no atomics; the two waves of a
-// channel block add the key halves in the same order, so they agree bit for
-// bit.  Splitting a sequence at a multiple of 16 tokens gives bit-identical
-// results; other split points agree within rounding (the chunk grid moves).
+// gfx950 mapping.
+// * gdn_scan_prep (parallel over sequence x chunk x key head):
+//   - k.k and q.k of the chunk on fp32 MFMA, once per key head;
+//   - K, Q (16 tokens x 128 keys) and K^T split into hi/lo fp16 and laid out
+//     in the exact per-lane operand order of the chunk kernel's MFMAs
+//     ("key-head slot", 24 KB per chunk);
+//   - per value head: the decays, T = (I + A)^-1 by forward substitution
+//     (one column per lane, in registers), M, Lam, beta and the last-row
+//     decays, T and M split and laid out as MFMA operands ("value-head slot").
+// * gdn_scan_chunk (sequential over chunks): a block of 4 waves owns 64 value
+//   channels of one (sequence, value head), one wave per SIMD (two waves per
+//   SIMD measured slower: the SIMD's MFMA and VALU issue are the limit, not
+//   latency alone); each wave holds 16 channels x all 128 keys of the state in
+//   MFMA accumulator layout (32 VGPRs/lane), so no partial sums cross waves.
+//   Per chunk and wave:
+//     K S^T, Q S^T    12 + 12  v_mfma_f32_16x16x32_f16 (3 split terms x 4 key steps)
+//     U = T B          3       v_mfma_f32_16x16x16_f16
+//     O = Lam R + M U  3       v_mfma_f32_16x16x16_f16
+//     S' = Lam_last S + K^T (D U)  24  v_mfma_f32_16x16x16_f16 (8 key blocks)
+//   Every product consumes the accumulator layout the previous one produced
+//   (the contraction index is permuted consistently, and the prep kernel packs
+//   K, Q and K^T in that order), so the state never leaves registers.
+//   The block stages the next chunk's slots and v through LDS (double
+//   buffered, loaded one chunk ahead); one barrier per chunk.
+// * Block order is XCD-aware: blocks are dealt round-robin to the 8 XCDs, so
+//   the index is permuted to give each XCD whole key-head groups, whose
+//   key-head slots are then shared in one L2.
+//
+// Determinism: fixed-order MFMA chains, no atomics.  Splitting a sequence at a
+// multiple of 16 tokens gives bit-identical results; other split points agree
+// within rounding (the chunk grid moves).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -56,28 +71,92 @@
 namespace gdn {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-constexpr int CT = 16;    // tokens per chunk
-constexpr int KS = 132;   // LDS row stride of the K/Q chunk (padded)
-// prep slot layout (floats)
-constexpr int OFF_T = 0;      // T = (I + A)^-1, [t][s]
-constexpr int OFF_M = 256;    // M / sqrt(dk), [t][s]
-constexpr int OFF_LAM = 512;  // Lam_t
-constexpr int OFF_LAMS = 528; // Lam_t / sqrt(dk)
-constexpr int OFF_BETA = 544; // beta_t (0 past the chunk's end)
-constexpr int OFF_W = 560;    // D[last][s] (0 past the end)
-constexpr int OFF_LAST = 576; // Lam_last
-static_assert(SCAN_SLOT_FLOATS >= 580 && SCAN_SLOT_FLOATS % 4 == 0, "slot too small");
+constexpr int CT = 16;           // tokens per chunk
+constexpr int KS = 132;          // LDS row stride of the fp32 K/Q chunk in prep
+constexpr float KQ_SCALE = 16.f; // k and q scale before the fp16 split (exact)
+constexpr float SCALE = 0.08838834764831845f;  // 1 / sqrt(128)
 
-__device__ __forceinline__ f4 mfma4(float a, float b, f4 c)
+// key-head slot, in fp16 elements
+constexpr int KH_KP = 0;     // [4 key steps][2 hi/lo][64 lanes][8]  K for K S^T
+constexpr int KH_QP = 4096;  // same for Q
+constexpr int KH_KT = 8192;  // [8 key blocks][2][64 lanes][4]       K^T for the update
+static_assert(SCAN_KH_FLOATS * 2 == 12288, "key-head slot size");
+// value-head slot, in floats
+constexpr int VH_TP = 0;       // [2][64 lanes][4] fp16  T   (256 floats)
+constexpr int VH_MP = 256;     // [2][64 lanes][4] fp16  M   (256 floats)
+constexpr int VH_LAM = 512;    // Lam_t / 256 (k, q and the state each carry a factor 16)
+constexpr int VH_BETA = 528;   // beta_t (0 past the chunk's end)
+constexpr int VH_W = 544;      // D[last][s] (0 past the end)
+constexpr int VH_LAST = 560;   // Lam_last
+static_assert(SCAN_SLOT_FLOATS >= 564 && SCAN_SLOT_FLOATS % 4 == 0, "value-head slot size");
+
+__device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c)
 {
-    // D[i][j] += sum_k A[i][k] B[k][j], 16x16x4: lane l supplies A[l%16][l/16]
-    // and B[l/16][l%16]; D[4(l/16)+r][l%16] comes back in component r.
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// D += A B, 16x16x16: lane l supplies A[l%16][4(l/16)+e] and B[4(l/16)+e][l%16];
+// D[4(l/16)+r][l%16] comes back in component r.
+__device__ __forceinline__ f4 mfma_k16(h4 a, h4 b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+// 16x16x32: A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], same D layout.
+__device__ __forceinline__ f4 mfma_k32(h8 a, h8 b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
-// Workspace slot of chunk c of sequence n (cu0 = cu[n]); injective, and
-// below total_T / 16 + n_seq.
+// x = hi + lo + O(2^-22 |x|): hi = fp16(x) rounded to nearest, lo = fp16(x - hi).
+// x - hi is formed exactly inside one fused multiply-add and rounded once to
+// fp16 (gfx950's mixed-precision FMA takes the fp16 hi and the fp32 x as they
+// are), two lanes' worth of lo per 32-bit register.
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1)
+{
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(r)
+        : "v"(hi2), "v"(x0), "v"(x1));
+    return r;
+}
+__device__ __forceinline__ uint32_t hi_pair(float x0, float x1)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 v = {(_Float16)x0, (_Float16)x1};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void split4(const f4 x, h4 &hi, h4 &lo)
+{
+    u2 h, l;
+    h[0] = hi_pair(x[0], x[1]);
+    h[1] = hi_pair(x[2], x[3]);
+    l[0] = lo_pair(h[0], x[0], x[1]);
+    l[1] = lo_pair(h[1], x[2], x[3]);
+    hi = __builtin_bit_cast(h4, h);
+    lo = __builtin_bit_cast(h4, l);
+}
+__device__ __forceinline__ void split8(const f4 a, const f4 b, h8 &hi, h8 &lo)
+{
+    u4 h, l;
+    h[0] = hi_pair(a[0], a[1]);
+    h[1] = hi_pair(a[2], a[3]);
+    h[2] = hi_pair(b[0], b[1]);
+    h[3] = hi_pair(b[2], b[3]);
+    l[0] = lo_pair(h[0], a[0], a[1]);
+    l[1] = lo_pair(h[1], a[2], a[3]);
+    l[2] = lo_pair(h[2], b[0], b[1]);
+    l[3] = lo_pair(h[3], b[2], b[3]);
+    hi = __builtin_bit_cast(h8, h);
+    lo = __builtin_bit_cast(h8, l);
+}
+
+// Slot of chunk c of sequence n (cu0 = cu[n]); injective, and below
+// total_T / 16 + n_seq.
 __device__ __forceinline__ int64_t chunk_slot(int cu0, int n, int c)
 {
     return (int64_t)(cu0 >> 4) + c + n;
@@ -85,6 +164,7 @@ __device__ __forceinline__ int64_t chunk_slot(int cu0, int n, int c)
 
 struct PrepDims {
     int hk, hv, G, n_chunk_max;
+    int64_t vh_base;  // float offset of the value-head slots in the workspace
 };
 
 __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
@@ -94,9 +174,11 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
     __shared__ float sKK[CT][CT + 1];
     __shared__ float sQK[CT][CT + 1];
     __shared__ float sA[4][CT][CT + 1];
+    __shared__ float sTm[4][CT][CT + 1];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
     const int n = blockIdx.x / d.n_chunk_max;
     const int c = blockIdx.x - n * d.n_chunk_max;
     const int j = blockIdx.y;
@@ -107,6 +189,7 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
     const int64_t tb = (int64_t)cu0 + c * CT;
     const int hk = d.hk, hv = d.hv;
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const int64_t slot = chunk_slot(cu0, n, c);
 
     // stage the chunk's k and q rows of key head j (zero past the end)
 #pragma unroll
@@ -122,7 +205,41 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
     }
     __syncthreads();
 
-    // wave 0: K K^T, wave 1: Q K^T (16 x 16 over 128 keys, 32 MFMA each)
+    // ---- key-head slot: K, Q and K^T split and packed in operand order ----
+    _Float16 *kh = reinterpret_cast<_Float16 *>(p.ws + (slot * hk + j) * SCAN_KH_FLOATS);
+    {
+        // K S^T step s, lane L = 16 kk + t holds keys 32 s + 16 (e / 4) + 4 kk + e % 4
+        const int s = wave, L = lane, t = l16;
+        f4 ka, kb, qa, qb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ka[e] = KQ_SCALE * sK[t][32 * s + 4 * kk + e];
+            kb[e] = KQ_SCALE * sK[t][32 * s + 16 + 4 * kk + e];
+            qa[e] = KQ_SCALE * sQ[t][32 * s + 4 * kk + e];
+            qb[e] = KQ_SCALE * sQ[t][32 * s + 16 + 4 * kk + e];
+        }
+        h8 hi, lo;
+        split8(ka, kb, hi, lo);
+        *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 0) * 64 + L) * 8) = hi;
+        *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 1) * 64 + L) * 8) = lo;
+        split8(qa, qb, hi, lo);
+        *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + L) * 8) = hi;
+        *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + L) * 8) = lo;
+        // K^T block b, lane L = 16 kk + m holds K[4 kk + e][16 b + m]
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int b = 2 * wave + m2;
+            f4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = KQ_SCALE * sK[4 * kk + e][16 * b + l16];
+            h4 h, l;
+            split4(x, h, l);
+            *reinterpret_cast<h4 *>(kh + KH_KT + ((b * 2 + 0) * 64 + L) * 4) = h;
+            *reinterpret_cast<h4 *>(kh + KH_KT + ((b * 2 + 1) * 64 + L) * 4) = l;
+        }
+    }
+
+    // wave 0: K K^T, wave 1: Q K^T (16 x 16 over 128 keys, fp32 MFMA)
     if (wave < 2) {
         const float(*X)[KS] = wave == 0 ? sK : sQ;
         f4 acc = z4;
@@ -131,7 +248,7 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
             const f4 xa = *reinterpret_cast<const f4 *>(&X[l16][16 * jb + 4 * kk]);
             const f4 kb = *reinterpret_cast<const f4 *>(&sK[l16][16 * jb + 4 * kk]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc = mfma4(xa[r], kb[r], acc);
+            for (int r = 0; r < 4; ++r) acc = mfma_f32(xa[r], kb[r], acc);
         }
         float(*O)[CT + 1] = wave == 0 ? sKK : sQK;
 #pragma unroll
@@ -139,10 +256,10 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
     }
     __syncthreads();
 
-    const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+    // ---- value-head slots ------------------------------------------------
     for (int gh = wave; gh < d.G; gh += 4) {
         const int h = j * d.G + gh;
-        float *slot = p.ws + (chunk_slot(cu0, n, c) * hv + h) * SCAN_SLOT_FLOATS;
+        float *vs = p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS;
         float gv[CT], bv[CT];
 #pragma unroll
         for (int t = 0; t < CT; ++t) {
@@ -152,7 +269,7 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
             gv[t] = t < nv ? gg : 0.f;
             bv[t] = t < nv ? bb : 0.f;
         }
-        // A (to LDS) and M (to the slot): entry (t, s), four per lane
+        // A (to LDS) by entries e = lane + 64 m
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int e = lane + 64 * m;
@@ -161,10 +278,26 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 #pragma unroll
             for (int r = 1; r < CT; ++r)
                 if (r > s && r <= t) sum += gv[r];
-            const float dec = expf(sum);
-            const bool live = t < nv;
-            sA[wave][t][s] = (live && s < t) ? bv[t] * dec * sKK[t][s] : 0.f;
-            slot[OFF_M + e] = (live && s <= t) ? dec * sQK[t][s] * scale : 0.f;
+            sA[wave][t][s] = (t < nv && s < t) ? bv[t] * expf(sum) * sKK[t][s] : 0.f;
+        }
+        // M in operand order: lane L = 16 kk + t holds M[t][4 kk + e]
+        {
+            const int t = l16;
+            f4 mv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 4 * kk + e;
+                float sum = 0.f;
+#pragma unroll
+                for (int r = 1; r < CT; ++r)
+                    if (r > s && r <= t) sum += gv[r];
+                mv[e] = (t < nv && s <= t) ? expf(sum) * sQK[t][s] : 0.f;
+            }
+            h4 hi, lo;
+            split4(mv, hi, lo);
+            _Float16 *mp = reinterpret_cast<_Float16 *>(vs + VH_MP);
+            *reinterpret_cast<h4 *>(mp + (0 * 64 + lane) * 4) = hi;
+            *reinterpret_cast<h4 *>(mp + (1 * 64 + lane) * 4) = lo;
         }
         if (lane < CT) {
             const int t = lane;
@@ -175,11 +308,10 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
                 if (r > t && r < nv) wdec += gv[r];
             }
             const float L = t < nv ? expf(lam) : 0.f;
-            slot[OFF_LAM + t] = L;
-            slot[OFF_LAMS + t] = L * scale;
-            slot[OFF_BETA + t] = bv[t];
-            slot[OFF_W + t] = t < nv ? expf(wdec) : 0.f;
-            if (t == nv - 1) slot[OFF_LAST] = L;
+            vs[VH_LAM + t] = L * (1.f / (KQ_SCALE * KQ_SCALE));
+            vs[VH_BETA + t] = bv[t];
+            vs[VH_W + t] = t < nv ? expf(wdec) : 0.f;
+            if (t == nv - 1) vs[VH_LAST] = L;
         }
         // the wave's A writes must land before its lanes read them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -197,7 +329,21 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
                 Tc[t] = acc;
             }
 #pragma unroll
-            for (int t = 0; t < CT; ++t) slot[OFF_T + t * CT + s] = Tc[t];
+            for (int t = 0; t < CT; ++t) sTm[wave][t][s] = Tc[t];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+            // T in operand order: lane L = 16 kk + t holds T[t][4 kk + e]
+            f4 tv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tv[e] = sTm[wave][l16][4 * kk + e];
+            h4 hi, lo;
+            split4(tv, hi, lo);
+            _Float16 *tp = reinterpret_cast<_Float16 *>(vs + VH_TP);
+            *reinterpret_cast<h4 *>(tp + (0 * 64 + lane) * 4) = hi;
+            *reinterpret_cast<h4 *>(tp + (1 * 64 + lane) * 4) = lo;
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -205,37 +351,33 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 
 struct ChunkDims {
     int hk, hv, G;
+    int64_t vh_base;
 };
 
-// LDS strides (floats): rows padded so 16 lanes reading 16 rows hit distinct
-// banks as far as a 16-byte read allows.
-constexpr int TS_ = 20;   // T, M and V^T rows
-constexpr int VEC = 80;   // Lam, Lam/sqrt(dk), beta, D[last][.], Lam_last
+constexpr int VT = 20;  // LDS row stride of v^T ([channel][token])
 
-__global__ __launch_bounds__(256) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
+constexpr int CHUNK_WAVES = 4;                 // half a value head: 4 x 16 channels
+constexpr int CHUNK_THREADS = 64 * CHUNK_WAVES;
+constexpr int CHUNK_ROWS = 16 * CHUNK_WAVES;    // value channels per block
+
+__global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
 {
-    // Staging buffers, indexed by chunk: K, V and the prep data are read after
-    // the chunk's one barrier, so they rotate through 3 buffers; Q is read
-    // only before it, so 2 suffice.  The partial sums rotate through 2.
-    __shared__ __attribute__((aligned(16))) float sK[3][CT][KS];
-    __shared__ __attribute__((aligned(16))) float sQ[2][CT][KS];
-    __shared__ __attribute__((aligned(16))) float sV[3][32][TS_];   // v, [channel][token]
-    __shared__ __attribute__((aligned(16))) float sT[3][CT][TS_];
-    __shared__ __attribute__((aligned(16))) float sM[3][CT][TS_];
-    __shared__ __attribute__((aligned(16))) float sVec[3][VEC];
-    __shared__ __attribute__((aligned(16))) float sX[2][4][2][64][4];  // partial P, R
+    // double-buffered staging: key-head slot, value-head slot, v^T of the head
+    __shared__ __attribute__((aligned(16))) float sKH[2][SCAN_KH_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sVH[2][SCAN_SLOT_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sV[2][CHUNK_ROWS][VT];
 
     const int tid = threadIdx.x;
-    // wave index as a scalar: everything derived from it stays in SGPRs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
 
-    // XCD-aware work index -> (sequence n, value head h, 32-channel block rb)
+    // XCD-aware work index -> (sequence n, value head h, channel block rb)
+    constexpr int RB = 128 / CHUNK_ROWS;
     const int nb = gridDim.x;
     int w = (int)blockIdx.x;
     if ((nb & 7) == 0) w = (w & 7) * (nb >> 3) + (w >> 3);
-    const int rb = w & 3;
-    w >>= 2;
+    const int rb = w % RB;
+    w /= RB;
     const int h = w % d.hv;
     const int n = w / d.hv;
     const int j = h / d.G;
@@ -244,198 +386,170 @@ __global__ __launch_bounds__(256) void scan_chunk_kernel(ScanArgs p, ChunkDims d
     const int cu0 = p.cu[n];
     const int T_n = p.cu[n + 1] - cu0;
     if (T_n <= 0) return;
+    const int row = rb * CHUNK_ROWS + wave * 16 + l16;
 
-    const int rs = wave >> 1;  // 16-channel sub-block
-    const int jh = wave & 1;   // key half: key blocks 4 jh .. 4 jh + 3
-    const int row = rb * 32 + rs * 16 + l16;
-    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
-
-    // state quarter, accumulator layout: S4[b][r] = S[row][16 (4 jh + b) + 4 kk + r]
-    float *Srow = p.state + (((int64_t)n * hv + h) * 128 + row) * 128 + 64 * jh + 4 * kk;
-    f4 S4[4];
+    // state x 16 (exact), accumulator layout: S4[b][r] = 16 S[row][16 b + 4 kk + r].
+    // With k and q also x16, every split operand and product stays well above
+    // the fp16 subnormal range; Lam carries the 1/256 back.
+    float *Srow = p.state + (((int64_t)n * hv + h) * 128 + row) * 128 + 4 * kk;
+    f4 S4[8];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b);
+    for (int b = 0; b < 8; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b) * KQ_SCALE;
 
-    // Staging roles: k and q rows by all 256 threads (2 float4 each), v by
-    // threads 0..127, the prep slot (T, M: 128 float4; the vectors: 20) by
-    // threads 96..243.
-    constexpr int SLOT_T0 = 96;
-    const int tA = tid >> 5, tB = tA + 8, colK = (tid & 31) * 4;
-    const int tV = tid >> 3, chV = (tid & 7) * 4;  // tid < 128
-    const int fP = tid - SLOT_T0;                  // prep float4 index, 0..147
-    f4 rkA = z4, rkB = z4, rqA = z4, rqB = z4, rv = z4, rp = z4;
     const int n_chunks = (T_n + CT - 1) / CT;
-    const uint32_t kstride = (uint32_t)hk * 128;   // floats per token row of qn/kn
     const uint32_t vstride = (uint32_t)hv * 128;
-
-    // Global loads only.  Rows past the sequence's end are read from its last
-    // token instead (always valid memory) and then carry no weight: the prep
-    // slot gives them beta = Lam = 0 and zero decay weights, and T is the
-    // identity there, so they add exactly nothing to U, O or the state.
-    // Addresses are a uniform base (SGPRs) plus a 32-bit byte offset per lane,
-    // the form the global loads take directly.
+    // staging roles: the key-head slot (1536 float4) KH_PER per thread, the
+    // value-head slot (144 float4) by threads 0..143, v (16 tokens x the
+    // block's channels) one float4 per thread
+    constexpr int KH_PER = SCAN_KH_FLOATS / 4 / CHUNK_THREADS;
+    static_assert(KH_PER * 4 * CHUNK_THREADS == SCAN_KH_FLOATS, "key-head slot staging");
+    static_assert(CT * CHUNK_ROWS == 4 * CHUNK_THREADS, "one float4 of v per thread");
+    const int tV = tid / (CHUNK_ROWS / 4), chV = (tid % (CHUNK_ROWS / 4)) * 4;
+    f4 rk[KH_PER], rvh = {0.f, 0.f, 0.f, 0.f}, rv;
     auto ld4 = [](const float *base, uint32_t byte_off) {
         return *reinterpret_cast<const f4 *>(reinterpret_cast<const char *>(base) + byte_off);
     };
+    // Rows past the sequence's end read its last token (valid memory); the
+    // slots give them zero weight (beta = Lam = 0, identity rows of T, zero
+    // k and q), so they add exactly nothing.
     auto fetch = [&](int c) {
         const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
         const int nv = min(CT, T_n - c * CT);
-        const float *kc = p.kn + (tb * hk + j) * 128;
-        const float *qc = p.qn + (tb * hk + j) * 128;
-        const uint32_t oA = ((uint32_t)min(tA, nv - 1) * kstride + colK) * 4u;
-        const uint32_t oB = ((uint32_t)min(tB, nv - 1) * kstride + colK) * 4u;
-        rkA = ld4(kc, oA);
-        rqA = ld4(qc, oA);
-        rkB = ld4(kc, oB);
-        rqB = ld4(qc, oB);
-        if (tid < 128)
-            rv = ld4(p.vc + (tb * hv + h) * 128 + rb * 32,
-                     ((uint32_t)min(tV, nv - 1) * vstride + chV) * 4u);
-        if (fP >= 0 && fP < 148)
-            rp = ld4(p.ws + (chunk_slot(cu0, n, c) * hv + h) * SCAN_SLOT_FLOATS, 16u * fP);
+        const int64_t slot = chunk_slot(cu0, n, c);
+        const float *khs = p.ws + (slot * hk + j) * SCAN_KH_FLOATS;
+#pragma unroll
+        for (int m = 0; m < KH_PER; ++m) rk[m] = ld4(khs, 16u * (tid + CHUNK_THREADS * m));
+        if (tid < SCAN_SLOT_FLOATS / 4)
+            rvh = ld4(p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS, 16u * tid);
+        rv = ld4(p.vc + (tb * hv + h) * 128 + rb * CHUNK_ROWS,
+                 ((uint32_t)min(tV, nv - 1) * vstride + chV) * 4u);
     };
-    // registers -> the LDS buffers (b3, b2) of the chunk they hold
-    auto stage = [&](auto b3c, auto b2c) {
-        constexpr int b3 = decltype(b3c)::value, b2 = decltype(b2c)::value;
-        *reinterpret_cast<f4 *>(&sK[b3][tA][colK]) = rkA;
-        *reinterpret_cast<f4 *>(&sK[b3][tB][colK]) = rkB;
-        *reinterpret_cast<f4 *>(&sQ[b2][tA][colK]) = rqA;
-        *reinterpret_cast<f4 *>(&sQ[b2][tB][colK]) = rqB;
-        if (tid < 128) {
-            sV[b3][chV + 0][tV] = rv[0];
-            sV[b3][chV + 1][tV] = rv[1];
-            sV[b3][chV + 2][tV] = rv[2];
-            sV[b3][chV + 3][tV] = rv[3];
-        }
-        if (fP >= 0 && fP < 64)
-            *reinterpret_cast<f4 *>(&sT[b3][fP >> 2][(fP & 3) * 4]) = rp;
-        else if (fP >= 64 && fP < 128)
-            *reinterpret_cast<f4 *>(&sM[b3][(fP - 64) >> 2][(fP & 3) * 4]) = rp;
-        else if (fP >= 128 && fP < 148)
-            *reinterpret_cast<f4 *>(&sVec[b3][4 * (fP - 128)]) = rp;
+    auto stage = [&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+#pragma unroll
+        for (int m = 0; m < KH_PER; ++m)
+            *reinterpret_cast<f4 *>(&sKH[b][4 * (tid + CHUNK_THREADS * m)]) = rk[m];
+        if (tid < SCAN_SLOT_FLOATS / 4) *reinterpret_cast<f4 *>(&sVH[b][4 * tid]) = rvh;
+        sV[b][chV + 0][tV] = rv[0];
+        sV[b][chV + 1][tV] = rv[1];
+        sV[b][chV + 2][tV] = rv[2];
+        sV[b][chV + 3][tV] = rv[3];
     };
 
-    // One chunk, with its LDS buffers (b3, b2) known at compile time.
-    auto step = [&](auto b3c, auto b2c, int c) {
-        constexpr int b3 = decltype(b3c)::value, b2 = decltype(b2c)::value;
+    auto step = [&](auto bc, int c) {
+        constexpr int b = decltype(bc)::value;
         const int nv = min(CT, T_n - c * CT);
         const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
-        // next chunk to LDS (its buffers were last read two chunks ago, before
-        // the previous barrier), then start loading the one after
         if (c + 1 < n_chunks) {
-            stage(std::integral_constant<int, (b3 + 1) % 3>{}, std::integral_constant<int, b2 ^ 1>{});
+            stage(std::integral_constant<int, b ^ 1>{});
             if (c + 2 < n_chunks) fetch(c + 2);
         }
+        const _Float16 *kh = reinterpret_cast<const _Float16 *>(sKH[b]);
+        const float *vh = sVH[b];
+        // operands of this chunk
+        h8 kph[4], kpl[4], qph[4], qpl[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            kph[s] = *reinterpret_cast<const h8 *>(kh + KH_KP + ((s * 2 + 0) * 64 + lane) * 8);
+            kpl[s] = *reinterpret_cast<const h8 *>(kh + KH_KP + ((s * 2 + 1) * 64 + lane) * 8);
+            qph[s] = *reinterpret_cast<const h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + lane) * 8);
+            qpl[s] = *reinterpret_cast<const h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + lane) * 8);
+        }
+        const _Float16 *tp = reinterpret_cast<const _Float16 *>(vh + VH_TP);
+        const _Float16 *mp = reinterpret_cast<const _Float16 *>(vh + VH_MP);
+        const h4 tph = *reinterpret_cast<const h4 *>(tp + lane * 4);
+        const h4 tpl = *reinterpret_cast<const h4 *>(tp + (64 + lane) * 4);
+        const h4 mph = *reinterpret_cast<const h4 *>(mp + lane * 4);
+        const h4 mpl = *reinterpret_cast<const h4 *>(mp + (64 + lane) * 4);
+        const f4 lam = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
+        const f4 bet = *reinterpret_cast<const f4 *>(vh + VH_BETA + 4 * kk);
+        const f4 wu = *reinterpret_cast<const f4 *>(vh + VH_W + 4 * kk);
+        const float last = vh[VH_LAST];
+        const f4 vv = *reinterpret_cast<const f4 *>(&sV[b][wave * 16 + l16][4 * kk]);
 
-        // Every LDS operand of this chunk except the partner's partial sums is
-        // in place already: read them all before the barrier, so that after it
-        // only the exchange waits on LDS.
-        f4 ka[4], qa[4];
+        // P^T = K S^T and R^T = Q S^T (x256), three split terms each
+        f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh, Rhh = Phh, Rhl = Phh, Rlh = Phh;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int col = 16 * (4 * jh + b) + 4 * kk;
-            ka[b] = *reinterpret_cast<const f4 *>(&sK[b3][l16][col]);
-            qa[b] = *reinterpret_cast<const f4 *>(&sQ[b2][l16][col]);
+        for (int s = 0; s < 4; ++s) {
+            h8 sh, sl;
+            split8(S4[2 * s], S4[2 * s + 1], sh, sl);
+            Phh = mfma_k32(kph[s], sh, Phh);
+            Rhh = mfma_k32(qph[s], sh, Rhh);
+            Phl = mfma_k32(kph[s], sl, Phl);
+            Rhl = mfma_k32(qph[s], sl, Rhl);
+            Plh = mfma_k32(kpl[s], sh, Plh);
+            Rlh = mfma_k32(qpl[s], sh, Rlh);
         }
-        const float *vec = sVec[b3];
-        const f4 lam = *reinterpret_cast<const f4 *>(vec + 4 * kk);
-        const f4 lams = *reinterpret_cast<const f4 *>(vec + 16 + 4 * kk);
-        const f4 bet = *reinterpret_cast<const f4 *>(vec + 32 + 4 * kk);
-        const f4 wv = *reinterpret_cast<const f4 *>(vec + 48 + 4 * kk);
-        const float last = vec[64];
-        const f4 vv = *reinterpret_cast<const f4 *>(&sV[b3][rs * 16 + l16][4 * kk]);
-        const f4 trow = *reinterpret_cast<const f4 *>(&sT[b3][l16][4 * kk]);
-        const f4 mrow = *reinterpret_cast<const f4 *>(&sM[b3][l16][4 * kk]);
-        // A operand of the state update, K^T: key 16 (4 jh + b) + l16, token 4 kk + r
-        float ak[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) ak[r][b] = sK[b3][4 * kk + r][16 * (4 * jh + b) + l16];
-        }
-
-        // partial P^T = K S0^T and R^T = Q S0^T over this wave's 64 keys
-        f4 P = z4, R = z4;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                P = mfma4(ka[b][r], S4[b][r], P);
-                R = mfma4(qa[b][r], S4[b][r], R);
-            }
-        }
-        f4 C[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) C[b] = S4[b] * last;
-        *reinterpret_cast<f4 *>(&sX[b2][wave][0][lane][0]) = P;
-        *reinterpret_cast<f4 *>(&sX[b2][wave][1][lane][0]) = R;
-        __syncthreads();  // the one barrier per chunk
-        {
-            // both waves of the pair add key half 0 + key half 1 (same bits)
-            const f4 Po = *reinterpret_cast<const f4 *>(&sX[b2][wave ^ 1][0][lane][0]);
-            const f4 Ro = *reinterpret_cast<const f4 *>(&sX[b2][wave ^ 1][1][lane][0]);
-            P = jh == 0 ? P + Po : Po + P;
-            R = jh == 0 ? R + Ro : Ro + R;
-        }
+        const f4 P = (Phh + Phl) + Plh;
+        const f4 R = (Rhh + Rhl) + Rlh;
         // B = beta (V - Lam P), component r is token 4 kk + r, channel l16
         f4 Bm;
 #pragma unroll
         for (int r = 0; r < 4; ++r) Bm[r] = bet[r] * (vv[r] - lam[r] * P[r]);
+        h4 bh, bl;
+        split4(Bm, bh, bl);
         // U = T B
-        f4 U = z4;
+        f4 U = {0.f, 0.f, 0.f, 0.f};
+        U = mfma_k16(tph, bh, U);
+        U = mfma_k16(tph, bl, U);
+        U = mfma_k16(tpl, bh, U);
+        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): 8 key blocks
+        h4 uwh, uwl;
+        split4(U * wu, uwh, uwl);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) U = mfma4(trow[r], Bm[r], U);
-        // S' = Lam_last S0 + K^T (D[last] U) on this wave's 64 keys
-        const f4 Uw = U * wv;
+        for (int kb = 0; kb < 8; ++kb) {
+            const h4 kth = *reinterpret_cast<const h4 *>(kh + KH_KT + ((kb * 2 + 0) * 64 + lane) * 4);
+            const h4 ktl = *reinterpret_cast<const h4 *>(kh + KH_KT + ((kb * 2 + 1) * 64 + lane) * 4);
+            f4 C = S4[kb] * last;
+            C = mfma_k16(kth, uwh, C);
+            C = mfma_k16(kth, uwl, C);
+            C = mfma_k16(ktl, uwh, C);
+            S4[kb] = C;
+        }
+        // O = (Lam R + M U) / sqrt(dk)
+        h4 uh, ul;
+        split4(U, uh, ul);
+        f4 O = lam * R;
+        O = mfma_k16(mph, uh, O);
+        O = mfma_k16(mph, ul, O);
+        O = mfma_k16(mpl, uh, O);
+        char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + wave * 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) C[b] = mfma4(ak[r][b], Uw[r], C[b]);
+            const int t = 4 * kk + r;
+            if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r] * SCALE;
         }
-        if (jh == 0) {
-            // O = Lam R + M U (both pre-scaled by 1/sqrt(dk))
-            f4 O = lams * R;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O = mfma4(mrow[r], U[r], O);
-            char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * 32 + rs * 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kk + r;
-                if (t < nv)
-                    *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r];
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) S4[b] = C[b];
+        __syncthreads();  // the chunk's buffers may be refilled after this
     };
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
     fetch(0);
-    stage(I0{}, I0{});
+    stage(I0{});
     if (n_chunks > 1) fetch(1);
     __syncthreads();
-    // unrolled by 6 = lcm(3, 2) so every buffer index is a constant
-    for (int c = 0; c < n_chunks; c += 6) {
-        step(I0{}, I0{}, c);
-        if (c + 1 < n_chunks) step(I1{}, I1{}, c + 1);
-        if (c + 2 < n_chunks) step(I2{}, I0{}, c + 2);
-        if (c + 3 < n_chunks) step(I0{}, I1{}, c + 3);
-        if (c + 4 < n_chunks) step(I1{}, I0{}, c + 4);
-        if (c + 5 < n_chunks) step(I2{}, I1{}, c + 5);
+    for (int c = 0; c < n_chunks; c += 2) {
+        step(I0{}, c);
+        if (c + 1 < n_chunks) step(I1{}, c + 1);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) *reinterpret_cast<f4 *>(Srow + 16 * b) = S4[b];
+    for (int b = 0; b < 8; ++b) *reinterpret_cast<f4 *>(Srow + 16 * b) = S4[b] * (1.f / KQ_SCALE);
+}
+
+static int64_t scan_slots(const gdn_shape &s)
+{
+    return s.total_T / CT + (int64_t)s.n_seq + 1;
 }
 
 hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
 {
+    const int64_t vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
     PrepDims pd;
     pd.hk = s.hk;
     pd.hv = s.hv;
     pd.G = s.hv / s.hk;
     pd.n_chunk_max = (int)((s.max_T + CT - 1) / CT);
+    pd.vh_base = vh_base;
     hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk),
                        dim3(256), 0, st, a, pd);
     hipError_t e = hipGetLastError();
@@ -444,15 +558,16 @@ hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
     cd.hk = s.hk;
     cd.hv = s.hv;
     cd.G = s.hv / s.hk;
-    const int64_t blocks = (int64_t)s.n_seq * s.hv * 4;
-    hipLaunchKernelGGL(scan_chunk_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, cd);
+    cd.vh_base = vh_base;
+    const int64_t blocks = (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS);
+    hipLaunchKernelGGL(scan_chunk_kernel, dim3((unsigned)blocks), dim3(CHUNK_THREADS), 0, st, a, cd);
     return hipGetLastError();
 }
 
 size_t scan_workspace_bytes(const gdn_shape &s)
 {
-    const size_t slots = (size_t)(s.total_T / CT) + (size_t)s.n_seq + 1;
-    return slots * (size_t)s.hv * SCAN_SLOT_FLOATS * sizeof(float);
+    return (size_t)scan_slots(s) * ((size_t)s.hk * SCAN_KH_FLOATS + (size_t)s.hv * SCAN_SLOT_FLOATS) *
+           sizeof(float);
 }
 
 } // namespace gdn

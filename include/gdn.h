@@ -159,8 +159,8 @@ int gdn_scan(const gdn_shape *shape, const int32_t *cu_seqlens,
              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of scratch gdn_scan needs for `shape` (0 if the shape is invalid):
- * one 2560-byte slot per (16-token chunk, value head), at most
- * (total_T/16 + n_seq + 1) * hv slots. */
+ * (total_T/16 + n_seq + 1) slots, each holding hk key-head parts of 24 KB and
+ * hv value-head parts of 2304 bytes. */
 size_t gdn_scan_workspace_bytes(const gdn_shape *shape);
 
 /*

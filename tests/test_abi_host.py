@@ -47,7 +47,8 @@ def test_workspace_bytes():
     s = shape(total_T=2048, max_T=2048)
     T = 2048
     r = lambda x: (x + 255) // 256 * 256
-    scan = (T // 16 + 1 + 1) * 48 * 640 * 4    # one 640-float slot per (chunk, value head)
+    per_slot = 16 * 24576 + 48 * 2304   # per 16-token chunk: key-head and value-head parts
+    scan = (T // 16 + 1 + 1) * per_slot
     assert B.gdn_scan_workspace_bytes(s) == scan
     want = 2 * r(T * 16 * 128 * 4) + r(T * 48 * 128 * 4) * 2 + 2 * r(T * 48 * 4) + r(scan)
     assert B.gdn_prefill_workspace_bytes(s) == want
@@ -55,7 +56,7 @@ def test_workspace_bytes():
     assert B.gdn_scan_workspace_bytes(shape(hv=47)) == 0
     # varlen: at most total_T / 16 + n_seq slots per value head
     v = shape(n_seq=4, total_T=27135, max_T=16384)
-    assert B.gdn_scan_workspace_bytes(v) == (27135 // 16 + 4 + 1) * 48 * 640 * 4
+    assert B.gdn_scan_workspace_bytes(v) == (27135 // 16 + 4 + 1) * per_slot
 
 
 def _pre(s, **over):

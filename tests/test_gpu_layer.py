@@ -109,9 +109,11 @@ def test_continuation_split_matches_whole_and_oracle(gpu):
     parity.check_y(y.reshape(T, w.hv, 128), ref["y"], w.out, what="y (split)")
     parity.check_state(state, ref["S"])
     parity.check_exact("hist (split)", hist.astype(np.float64), ref["hist"])
-    assert parity.check_state(state, np_(whole.state).astype(np.float64)) < 1e-5
+    # split and whole GPU runs agree to the same bars they each meet against
+    # the oracle
+    parity.check_state(state, np_(whole.state).astype(np.float64))
     d = np.abs(y.astype(np.float32) - np_(whole.y).astype(np.float32))
-    assert d.max() <= 2 * 2e-3
+    assert d.max() <= 2 * parity.Y_ABS
 
 
 def test_split_on_chunk_boundaries_is_bitwise(gpu):
