@@ -48,9 +48,11 @@
 //   MFMA accumulator layout (32 VGPRs/lane), so no partial sums cross waves.
 //   Per chunk and wave:
 //     K S^T, Q S^T    12 + 12  v_mfma_f32_16x16x32_f16 (3 split terms x 4 key steps)
-//     U = T B          3       v_mfma_f32_16x16x16_f16
-//     O = Lam R + M U  3       v_mfma_f32_16x16x16_f16
-//     S' = Lam_last S + K^T (D U)  24  v_mfma_f32_16x16x16_f16 (8 key blocks)
+//     U = T B          1 + 1    16x16x32 (hi.hi + lo.hi) + 16x16x16 (hi.lo)
+//     O = Lam R + M U  1 + 1    same
+//     S' = Lam_last S + K^T (D U)  8 + 8  same, per key block
+//   (over the 16 tokens of a chunk, two split terms share one 16x16x32 product:
+//   its contraction runs over the pair (term, token))
 //   Every product consumes the accumulator layout the previous one produced
 //   (the contraction index is permuted consistently, and the prep kernel packs
 //   K, Q and K^T in that order), so the state never leaves registers.
@@ -82,11 +84,11 @@ constexpr float SCALE = 0.08838834764831845f;  // 1 / sqrt(128)
 // key-head slot, in fp16 elements
 constexpr int KH_KP = 0;     // [4 key steps][2 hi/lo][64 lanes][8]  K for K S^T
 constexpr int KH_QP = 4096;  // same for Q
-constexpr int KH_KT = 8192;  // [8 key blocks][2][64 lanes][4]       K^T for the update
+constexpr int KH_KT = 8192;  // [8 key blocks][64 lanes][hi 4, lo 4]  K^T for the update
 static_assert(SCAN_KH_FLOATS * 2 == 12288, "key-head slot size");
 // value-head slot, in floats
-constexpr int VH_TP = 0;       // [2][64 lanes][4] fp16  T   (256 floats)
-constexpr int VH_MP = 256;     // [2][64 lanes][4] fp16  M   (256 floats)
+constexpr int VH_TP = 0;       // [64 lanes][hi 4, lo 4] fp16  T   (256 floats)
+constexpr int VH_MP = 256;     // [64 lanes][hi 4, lo 4] fp16  M   (256 floats)
 constexpr int VH_LAM = 512;    // Lam_t / 256 (k, q and the state each carry a factor 16)
 constexpr int VH_BETA = 528;   // beta_t (0 past the chunk's end)
 constexpr int VH_W = 544;      // D[last][s] (0 past the end)
@@ -109,51 +111,65 @@ __device__ __forceinline__ f4 mfma_k32(h8 a, h8 b, f4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// x = hi + lo + O(2^-22 |x|): hi = fp16(x) rounded to nearest, lo = fp16(x - hi).
-// x - hi is formed exactly inside one fused multiply-add and rounded once to
-// fp16 (gfx950's mixed-precision FMA takes the fp16 hi and the fp32 x as they
-// are), two lanes' worth of lo per 32-bit register.
+// x = hi + lo + O(2^-22 |x|): hi = fp16(x) rounded toward zero, lo = fp16(x - hi)
+// rounded to nearest (|lo| < ulp(hi), so lo keeps 11 more bits of x).
+// x - hi is exact in fp32 and is formed by one mixed-precision multiply-add
+// (v_fma_mix takes the fp16 hi as it is); m1 = -1 comes in at run time so
+// that the compiler keeps that form instead of converting hi back first.
+// hi comes from the conversion intrinsic, which the compiler neither fuses
+// with the product that made x nor recomputes: both uses of hi (the MFMA
+// operand and the lo) see one value, and the pair sums to x.  (A plain
+// fp16 cast may be fused with a preceding multiply into one rounding in one
+// use and not in the other.)  Plain compiler-visible code on purpose: these
+// values feed MFMA operands, and the compiler inserts the VALU/MFMA hazard
+// waits only for code it sees.
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1)
-{
-    uint32_t r;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=&v"(r)
-        : "v"(hi2), "v"(x0), "v"(x1));
-    return r;
-}
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t hi_pair(float x0, float x1)
 {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    h2 v = {(_Float16)x0, (_Float16)x1};
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
 }
-__device__ __forceinline__ void split4(const f4 x, h4 &hi, h4 &lo)
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1, float m1)
+{
+    const h2 h = __builtin_bit_cast(h2, hi2);
+    const h2 r = {(_Float16)__builtin_fmaf((float)h[0], m1, x0),
+                  (_Float16)__builtin_fmaf((float)h[1], m1, x1)};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ void split4(const f4 x, h4 &hi, h4 &lo, float m1)
 {
     u2 h, l;
     h[0] = hi_pair(x[0], x[1]);
     h[1] = hi_pair(x[2], x[3]);
-    l[0] = lo_pair(h[0], x[0], x[1]);
-    l[1] = lo_pair(h[1], x[2], x[3]);
+    l[0] = lo_pair(h[0], x[0], x[1], m1);
+    l[1] = lo_pair(h[1], x[2], x[3], m1);
     hi = __builtin_bit_cast(h4, h);
     lo = __builtin_bit_cast(h4, l);
 }
-__device__ __forceinline__ void split8(const f4 a, const f4 b, h8 &hi, h8 &lo)
+__device__ __forceinline__ void split8(const f4 a, const f4 b, h8 &hi, h8 &lo, float m1)
 {
     u4 h, l;
     h[0] = hi_pair(a[0], a[1]);
     h[1] = hi_pair(a[2], a[3]);
     h[2] = hi_pair(b[0], b[1]);
     h[3] = hi_pair(b[2], b[3]);
-    l[0] = lo_pair(h[0], a[0], a[1]);
-    l[1] = lo_pair(h[1], a[2], a[3]);
-    l[2] = lo_pair(h[2], b[0], b[1]);
-    l[3] = lo_pair(h[3], b[2], b[3]);
+    l[0] = lo_pair(h[0], a[0], a[1], m1);
+    l[1] = lo_pair(h[1], a[2], a[3], m1);
+    l[2] = lo_pair(h[2], b[0], b[1], m1);
+    l[3] = lo_pair(h[3], b[2], b[3], m1);
     hi = __builtin_bit_cast(h8, h);
     lo = __builtin_bit_cast(h8, l);
 }
+
+// (a, b) as one 8-element operand: in a 16x16x32 product the contraction
+// positions 8(l/16) + e take a for e < 4 and b for e >= 4, so
+// mfma_k32(cat(x1, x2), cat(y1, y2)) = x1 y1 + x2 y2 over 16-deep halves.
+__device__ __forceinline__ h8 cat(h4 a, h4 b)
+{
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ h4 lo_half(h8 a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3); }
 
 // Slot of chunk c of sequence n (cu0 = cu[n]); injective, and below
 // total_T / 16 + n_seq.
@@ -164,6 +180,7 @@ __device__ __forceinline__ int64_t chunk_slot(int cu0, int n, int c)
 
 struct PrepDims {
     int hk, hv, G, n_chunk_max;
+    float m1;         // -1 (see lo_pair)
     int64_t vh_base;  // float offset of the value-head slots in the workspace
 };
 
@@ -219,10 +236,10 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
             qb[e] = KQ_SCALE * sQ[t][32 * s + 16 + 4 * kk + e];
         }
         h8 hi, lo;
-        split8(ka, kb, hi, lo);
+        split8(ka, kb, hi, lo, d.m1);
         *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 0) * 64 + L) * 8) = hi;
         *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 1) * 64 + L) * 8) = lo;
-        split8(qa, qb, hi, lo);
+        split8(qa, qb, hi, lo, d.m1);
         *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + L) * 8) = hi;
         *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + L) * 8) = lo;
         // K^T block b, lane L = 16 kk + m holds K[4 kk + e][16 b + m]
@@ -233,9 +250,8 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = KQ_SCALE * sK[4 * kk + e][16 * b + l16];
             h4 h, l;
-            split4(x, h, l);
-            *reinterpret_cast<h4 *>(kh + KH_KT + ((b * 2 + 0) * 64 + L) * 4) = h;
-            *reinterpret_cast<h4 *>(kh + KH_KT + ((b * 2 + 1) * 64 + L) * 4) = l;
+            split4(x, h, l, d.m1);
+            *reinterpret_cast<h8 *>(kh + KH_KT + (b * 64 + L) * 8) = cat(h, l);
         }
     }
 
@@ -294,10 +310,8 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
                 mv[e] = (t < nv && s <= t) ? expf(sum) * sQK[t][s] : 0.f;
             }
             h4 hi, lo;
-            split4(mv, hi, lo);
-            _Float16 *mp = reinterpret_cast<_Float16 *>(vs + VH_MP);
-            *reinterpret_cast<h4 *>(mp + (0 * 64 + lane) * 4) = hi;
-            *reinterpret_cast<h4 *>(mp + (1 * 64 + lane) * 4) = lo;
+            split4(mv, hi, lo, d.m1);
+            *reinterpret_cast<h8 *>(reinterpret_cast<_Float16 *>(vs + VH_MP) + lane * 8) = cat(hi, lo);
         }
         if (lane < CT) {
             const int t = lane;
@@ -340,10 +354,8 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 #pragma unroll
             for (int e = 0; e < 4; ++e) tv[e] = sTm[wave][l16][4 * kk + e];
             h4 hi, lo;
-            split4(tv, hi, lo);
-            _Float16 *tp = reinterpret_cast<_Float16 *>(vs + VH_TP);
-            *reinterpret_cast<h4 *>(tp + (0 * 64 + lane) * 4) = hi;
-            *reinterpret_cast<h4 *>(tp + (1 * 64 + lane) * 4) = lo;
+            split4(tv, hi, lo, d.m1);
+            *reinterpret_cast<h8 *>(reinterpret_cast<_Float16 *>(vs + VH_TP) + lane * 8) = cat(hi, lo);
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -351,6 +363,7 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 
 struct ChunkDims {
     int hk, hv, G;
+    float m1;         // -1 (see lo_pair)
     int64_t vh_base;
 };
 
@@ -455,64 +468,61 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
             qph[s] = *reinterpret_cast<const h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + lane) * 8);
             qpl[s] = *reinterpret_cast<const h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + lane) * 8);
         }
-        const _Float16 *tp = reinterpret_cast<const _Float16 *>(vh + VH_TP);
-        const _Float16 *mp = reinterpret_cast<const _Float16 *>(vh + VH_MP);
-        const h4 tph = *reinterpret_cast<const h4 *>(tp + lane * 4);
-        const h4 tpl = *reinterpret_cast<const h4 *>(tp + (64 + lane) * 4);
-        const h4 mph = *reinterpret_cast<const h4 *>(mp + lane * 4);
-        const h4 mpl = *reinterpret_cast<const h4 *>(mp + (64 + lane) * 4);
+        const h8 tp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_TP) + lane * 8);
+        const h8 mp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
         const f4 lam = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
         const f4 bet = *reinterpret_cast<const f4 *>(vh + VH_BETA + 4 * kk);
         const f4 wu = *reinterpret_cast<const f4 *>(vh + VH_W + 4 * kk);
         const float last = vh[VH_LAST];
         const f4 vv = *reinterpret_cast<const f4 *>(&sV[b][wave * 16 + l16][4 * kk]);
 
-        // P^T = K S^T and R^T = Q S^T (x256), three split terms each
+        // P = K S^T and R = Q S^T (x256): three split terms each, P first
+        // (it heads the chain to the next state), R behind it
+        h8 sh[4], sl[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) split8(S4[2 * s], S4[2 * s + 1], sh[s], sl[s], d.m1);
         f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh, Rhh = Phh, Rhl = Phh, Rlh = Phh;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            h8 sh, sl;
-            split8(S4[2 * s], S4[2 * s + 1], sh, sl);
-            Phh = mfma_k32(kph[s], sh, Phh);
-            Rhh = mfma_k32(qph[s], sh, Rhh);
-            Phl = mfma_k32(kph[s], sl, Phl);
-            Rhl = mfma_k32(qph[s], sl, Rhl);
-            Plh = mfma_k32(kpl[s], sh, Plh);
-            Rlh = mfma_k32(qpl[s], sh, Rlh);
+            Phh = mfma_k32(kph[s], sh[s], Phh);
+            Phl = mfma_k32(kph[s], sl[s], Phl);
+            Plh = mfma_k32(kpl[s], sh[s], Plh);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Rhh = mfma_k32(qph[s], sh[s], Rhh);
+            Rhl = mfma_k32(qph[s], sl[s], Rhl);
+            Rlh = mfma_k32(qpl[s], sh[s], Rlh);
         }
         const f4 P = (Phh + Phl) + Plh;
-        const f4 R = (Rhh + Rhl) + Rlh;
         // B = beta (V - Lam P), component r is token 4 kk + r, channel l16
         f4 Bm;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Bm[r] = bet[r] * (vv[r] - lam[r] * P[r]);
+        for (int r = 0; r < 4; ++r) Bm[r] = bet[r] * __builtin_fmaf(-lam[r], P[r], vv[r]);
         h4 bh, bl;
-        split4(Bm, bh, bl);
-        // U = T B
-        f4 U = {0.f, 0.f, 0.f, 0.f};
-        U = mfma_k16(tph, bh, U);
-        U = mfma_k16(tph, bl, U);
-        U = mfma_k16(tpl, bh, U);
+        split4(Bm, bh, bl, d.m1);
+        // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo
+        const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+        const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4);
         // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): 8 key blocks
         h4 uwh, uwl;
-        split4(U * wu, uwh, uwl);
+        split4(U * wu, uwh, uwl, d.m1);
+        const h8 uww = cat(uwh, uwh);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            const h4 kth = *reinterpret_cast<const h4 *>(kh + KH_KT + ((kb * 2 + 0) * 64 + lane) * 4);
-            const h4 ktl = *reinterpret_cast<const h4 *>(kh + KH_KT + ((kb * 2 + 1) * 64 + lane) * 4);
+            const h8 kt = *reinterpret_cast<const h8 *>(kh + KH_KT + (kb * 64 + lane) * 8);
             f4 C = S4[kb] * last;
-            C = mfma_k16(kth, uwh, C);
-            C = mfma_k16(kth, uwl, C);
-            C = mfma_k16(ktl, uwh, C);
+            C = mfma_k32(kt, uww, C);
+            C = mfma_k16(lo_half(kt), uwl, C);
             S4[kb] = C;
         }
         // O = (Lam R + M U) / sqrt(dk)
+        const f4 R = (Rhh + Rhl) + Rlh;
         h4 uh, ul;
-        split4(U, uh, ul);
+        split4(U, uh, ul, d.m1);
         f4 O = lam * R;
-        O = mfma_k16(mph, uh, O);
-        O = mfma_k16(mph, ul, O);
-        O = mfma_k16(mpl, uh, O);
+        O = mfma_k32(mp, cat(uh, uh), O);
+        O = mfma_k16(lo_half(mp), ul, O);
         char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + wave * 16);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -550,6 +560,7 @@ hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
     pd.G = s.hv / s.hk;
     pd.n_chunk_max = (int)((s.max_T + CT - 1) / CT);
     pd.vh_base = vh_base;
+    pd.m1 = -1.f;
     hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk),
                        dim3(256), 0, st, a, pd);
     hipError_t e = hipGetLastError();
@@ -559,6 +570,7 @@ hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
     cd.hv = s.hv;
     cd.G = s.hv / s.hk;
     cd.vh_base = vh_base;
+    cd.m1 = -1.f;
     const int64_t blocks = (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS);
     hipLaunchKernelGGL(scan_chunk_kernel, dim3((unsigned)blocks), dim3(CHUNK_THREADS), 0, st, a, cd);
     return hipGetLastError();

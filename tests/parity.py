@@ -7,7 +7,12 @@ Bars (each written here once and used by every GPU test):
   one of the two fp16 neighbours of y_ref.
 - y stored as fp32: max |dy| <= 2e-3.
 - state: per (sequence, value head) ||S_gpu - S_ref||_F / ||S_ref||_F <= 1e-4.
-- o (fp32 scan output): the same 1e-4 relative Frobenius bar per value head.
+- o (fp32 scan output): the same 1e-4 relative Frobenius bar per value head,
+  and elementwise max|do| <= 2e-4 x RMS(o_ref) of the head.  The second bar
+  catches isolated bad elements that a Frobenius norm averages away: an
+  fp32-accurate product chain stays near 1e-5 x RMS per element, while one
+  product that loses the low half of a split operand (error ~2^-11 of a term)
+  lands near 2e-3 x RMS.
 - history: bit-exact (a copy of stored input rows).
 - pre intermediates (fp32, one short fp32 chain per element): qn, kn, vc and
   beta within 1e-5 relative + 1e-6 absolute; g (|g| up to ~80) 1e-5 relative.
@@ -19,6 +24,7 @@ import numpy as np
 Y_ABS = 2e-3
 STATE_REL = 1e-4
 O_REL = 1e-4
+O_MAX_REL = 2e-4
 PRE_RTOL, PRE_ATOL = 1e-5, 1e-6
 
 
@@ -101,6 +107,12 @@ def check_o(o_gpu, o_ref, heads=None) -> float:
     worst = float(r.max(initial=0.0))
     if not np.isfinite(worst) or worst > O_REL:
         _fail(f"o: worst per-head relative Frobenius error {worst:.3e} > {O_REL}")
+    d = np.abs(np.asarray(o_gpu, np.float64) - o_ref).max(axis=(0, 2))
+    rms = np.sqrt((np.asarray(o_ref, np.float64) ** 2).mean(axis=(0, 2)))
+    e = d / np.maximum(rms, 1e-300)
+    h = int(np.argmax(e)) if e.size else 0
+    if e.size and e[h] > O_MAX_REL:
+        _fail(f"o: head {h} max|do| = {d[h]:.3e} is {e[h]:.2e} x RMS(o_ref) > {O_MAX_REL}")
     return worst
 
 

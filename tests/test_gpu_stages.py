@@ -111,6 +111,33 @@ def test_scan_matches_oracle(gpu, case):
             assert np.array_equal(np_(state.t)[k], d["S0"][k])
 
 
+def test_scan_on_layer_intermediates(gpu):
+    # the scan fed with what the oracle's pre stage makes of a production-width
+    # layer (T = 1365, non-zero state, decays and gates from the layer's own
+    # parameters), rounded to the fp32 storage of the intermediates
+    w = synth.WORKLOADS["prod_continuation_fp16"]
+    inp = synth.layer_inputs(w)
+    cu = w.cu_seqlens()
+    pr = orc.pre(orc.Dims(w.hk, w.hv), cu, inp["qkv"], inp["conv_w"], inp["a"], inp["b"],
+                 inp["A_log"], inp["dt_bias"], inp["hist"], 1e-6)
+    f32 = {k: pr[k].astype(np.float32) for k in ("qn", "kn", "vc", "g", "beta")}
+    S0 = inp["S0"].astype(np.float32)
+    o_ref, S_ref = orc.scan(orc.Dims(w.hk, w.hv), cu, f32["qn"], f32["kn"], f32["vc"], f32["g"],
+                            f32["beta"], S0)
+    T, dev = int(cu[-1]), "cuda"
+    state = Guarded(S0.shape, F32, init=torch.from_numpy(S0))
+    o = Guarded((T, w.hv, 128), F32)
+    s = B.make_shape(w.hk, w.hv, 1, T, T, io="f32", out="f32")
+    ws = Guarded((B.gdn_scan_workspace_bytes(s) // 4,), F32)
+    banner("gdn_scan", w.name, f"T={T}")
+    B.gdn_scan(s, upload(cu, dev), *(upload(f32[k], dev) for k in ("qn", "kn", "vc", "g", "beta")),
+               state.t, o.t, ws.t)
+    torch.cuda.synchronize()
+    assert state.intact() and o.intact() and ws.intact()
+    parity.check_o(np_(o.t), o_ref)
+    parity.check_state(np_(state.t), S_ref)
+
+
 def test_scan_invariant_beta0_g0_keeps_state_bitwise(gpu):
     hk, hv, T = 16, 48, 40
     d = synth.scan_inputs(hk, hv, (T,), seed=(8,), s0_std=0.05)
