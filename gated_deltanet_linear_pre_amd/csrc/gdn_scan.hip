@@ -56,8 +56,8 @@
 //   Every product consumes the accumulator layout the previous one produced
 //   (the contraction index is permuted consistently, and the prep kernel packs
 //   K, Q and K^T in that order), so the state never leaves registers.
-//   The block stages the next chunk's slots and v through LDS (double
-//   buffered, loaded one chunk ahead); one barrier per chunk.
+//   A copy wave moves the chunk operands from global memory into LDS three
+//   chunks ahead (four LDS copies); one barrier per chunk.
 // * Block order is XCD-aware: blocks are dealt round-robin to the 8 XCDs, so
 //   the index is permuted to give each XCD whole key-head groups, whose
 //   key-head slots are then shared in one L2.
@@ -367,18 +367,37 @@ struct ChunkDims {
     int64_t vh_base;
 };
 
-constexpr int VT = 20;  // LDS row stride of v^T ([channel][token])
+// A block owns 32 value channels of one (sequence, value head): two row groups
+// of 16 channels, and each row group is shared by a pair of waves, one per half
+// of the 128 keys; each of these four compute waves holds its 16 x 64 quarter
+// of the block's state.  A fifth wave only copies operands into LDS.
+constexpr int CHUNK_WAVES = 4;                       // compute waves: 2 row groups x 2 key halves
+constexpr int CHUNK_THREADS = 64 * (CHUNK_WAVES + 1); // + the copy wave
+constexpr int CHUNK_ROWS = 32;                       // value channels per block
+constexpr int NBUF = 4;                              // LDS copies of a chunk's operands
 
-constexpr int CHUNK_WAVES = 4;                 // half a value head: 4 x 16 channels
-constexpr int CHUNK_THREADS = 64 * CHUNK_WAVES;
-constexpr int CHUNK_ROWS = 16 * CHUNK_WAVES;    // value channels per block
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt
+// left at their maximum, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Block-wide barrier ordering LDS only: global copies in flight stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
 {
-    // double-buffered staging: key-head slot, value-head slot, v^T of the head
-    __shared__ __attribute__((aligned(16))) float sKH[2][SCAN_KH_FLOATS];
-    __shared__ __attribute__((aligned(16))) float sVH[2][SCAN_SLOT_FLOATS];
-    __shared__ __attribute__((aligned(16))) float sV[2][CHUNK_ROWS][VT];
+    // operands of four chunks in flight: key-head slot, value-head slot, v
+    __shared__ __attribute__((aligned(16))) float sKH[NBUF][SCAN_KH_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sVH[NBUF][SCAN_SLOT_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sV[NBUF][CT][CHUNK_ROWS];
+    // partial K S^T of every compute wave, partial Q S^T of the upper-key waves
+    __shared__ __attribute__((aligned(16))) f4 sXP[2][CHUNK_WAVES][64];
+    __shared__ __attribute__((aligned(16))) f4 sXR[2][CHUNK_WAVES / 2][64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -399,102 +418,131 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
     const int cu0 = p.cu[n];
     const int T_n = p.cu[n + 1] - cu0;
     if (T_n <= 0) return;
-    const int row = rb * CHUNK_ROWS + wave * 16 + l16;
-
-    // state x 16 (exact), accumulator layout: S4[b][r] = 16 S[row][16 b + 4 kk + r].
-    // With k and q also x16, every split operand and product stays well above
-    // the fp16 subnormal range; Lam carries the 1/256 back.
-    float *Srow = p.state + (((int64_t)n * hv + h) * 128 + row) * 128 + 4 * kk;
-    f4 S4[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b) * KQ_SCALE;
-
     const int n_chunks = (T_n + CT - 1) / CT;
     const uint32_t vstride = (uint32_t)hv * 128;
-    // staging roles: the key-head slot (1536 float4) KH_PER per thread, the
-    // value-head slot (144 float4) by threads 0..143, v (16 tokens x the
-    // block's channels) one float4 per thread
-    constexpr int KH_PER = SCAN_KH_FLOATS / 4 / CHUNK_THREADS;
-    static_assert(KH_PER * 4 * CHUNK_THREADS == SCAN_KH_FLOATS, "key-head slot staging");
-    static_assert(CT * CHUNK_ROWS == 4 * CHUNK_THREADS, "one float4 of v per thread");
-    const int tV = tid / (CHUNK_ROWS / 4), chV = (tid % (CHUNK_ROWS / 4)) * 4;
-    f4 rk[KH_PER], rvh = {0.f, 0.f, 0.f, 0.f}, rv;
-    auto ld4 = [](const float *base, uint32_t byte_off) {
-        return *reinterpret_cast<const f4 *>(reinterpret_cast<const char *>(base) + byte_off);
-    };
-    // Rows past the sequence's end read its last token (valid memory); the
-    // slots give them zero weight (beta = Lam = 0, identity rows of T, zero
-    // k and q), so they add exactly nothing.
-    auto fetch = [&](int c) {
-        const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
-        const int nv = min(CT, T_n - c * CT);
-        const int64_t slot = chunk_slot(cu0, n, c);
-        const float *khs = p.ws + (slot * hk + j) * SCAN_KH_FLOATS;
-#pragma unroll
-        for (int m = 0; m < KH_PER; ++m) rk[m] = ld4(khs, 16u * (tid + CHUNK_THREADS * m));
-        if (tid < SCAN_SLOT_FLOATS / 4)
-            rvh = ld4(p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS, 16u * tid);
-        rv = ld4(p.vc + (tb * hv + h) * 128 + rb * CHUNK_ROWS,
-                 ((uint32_t)min(tV, nv - 1) * vstride + chV) * 4u);
-    };
-    auto stage = [&](auto bc) {
-        constexpr int b = decltype(bc)::value;
-#pragma unroll
-        for (int m = 0; m < KH_PER; ++m)
-            *reinterpret_cast<f4 *>(&sKH[b][4 * (tid + CHUNK_THREADS * m)]) = rk[m];
-        if (tid < SCAN_SLOT_FLOATS / 4) *reinterpret_cast<f4 *>(&sVH[b][4 * tid]) = rvh;
-        sV[b][chV + 0][tV] = rv[0];
-        sV[b][chV + 1][tV] = rv[1];
-        sV[b][chV + 2][tV] = rv[2];
-        sV[b][chV + 3][tV] = rv[3];
-    };
 
-    auto step = [&](auto bc, int c) {
-        constexpr int b = decltype(bc)::value;
+    if (wave == CHUNK_WAVES) {
+        // ---- copy wave: global -> LDS, three chunks ahead of the compute --
+        // global_load_lds_dwordx4 moves 1 KB per instruction (lane i lands at
+        // 16 i past the piece's LDS base) without passing through registers.
+        typedef const void __attribute__((address_space(1))) *gptr_t;
+        typedef void __attribute__((address_space(3))) *lptr_t;
+        constexpr int KH_PIECES = SCAN_KH_FLOATS * 4 / 1024;                       // 24
+        constexpr int VH_PIECES = (SCAN_SLOT_FLOATS * 4 + 1023) / 1024;             // 3
+        constexpr int VH_TAIL = (SCAN_SLOT_FLOATS * 4 - (VH_PIECES - 1) * 1024) / 16;  // 16 lanes
+        constexpr int V_PIECES = CT * CHUNK_ROWS * 4 / 1024;                        // 2
+        constexpr int V_LANES = CHUNK_ROWS / 4;                                     // lanes per token
+        constexpr int PER_CHUNK = KH_PIECES + VH_PIECES + V_PIECES;                 // copies per chunk
+        static_assert(V_PIECES * 1024 == CT * CHUNK_ROWS * 4, "v pieces");
+        static_assert(2 * PER_CHUNK <= 63, "vmcnt range");
+        auto copy16 = [](const float *src, float *lds_piece) {
+            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_piece, 16, 0, 0);
+        };
+        // Rows past the sequence's end read its last token (valid memory); the
+        // slots give them zero weight (beta = Lam = 0, identity rows of T, zero
+        // k and q), so they add exactly nothing.
+        auto issue = [&](int c) {
+            const int b = c & (NBUF - 1);
+            const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
+            const int nv = min(CT, T_n - c * CT);
+            const int64_t slot = chunk_slot(cu0, n, c);
+            const float *khs = p.ws + (slot * hk + j) * SCAN_KH_FLOATS + lane * 4;
+#pragma unroll
+            for (int m = 0; m < KH_PIECES; ++m) copy16(khs + m * 256, &sKH[b][m * 256]);
+            const float *vhs = p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS + lane * 4;
+#pragma unroll
+            for (int m = 0; m < VH_PIECES - 1; ++m) copy16(vhs + m * 256, &sVH[b][m * 256]);
+            if (lane < VH_TAIL) copy16(vhs + (VH_PIECES - 1) * 256, &sVH[b][(VH_PIECES - 1) * 256]);
+            const float *vb = p.vc + (tb * hv + h) * 128 + rb * CHUNK_ROWS + (lane % V_LANES) * 4;
+#pragma unroll
+            for (int m = 0; m < V_PIECES; ++m) {
+                const int t = m * (64 / V_LANES) + lane / V_LANES;
+                copy16(vb + (uint32_t)min(t, nv - 1) * vstride, &sV[b][m * (64 / V_LANES)][0]);
+            }
+        };
+        // Chunk c sits in LDS copy c % 4.  It is issued after the barrier of
+        // step c - 3 (the compute waves are then done with chunk c - 4) and
+        // waited for before the barrier of step c - 1; step c reads it.
+        for (int c = 0; c < 3 && c < n_chunks; ++c) issue(c);
+        if (n_chunks > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_CHUNK));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();
+        for (int c = 0; c < n_chunks; ++c) {
+            lds_barrier();
+            if (c + 3 < n_chunks) {
+                issue(c + 3);
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_CHUNK));  // chunk c + 2 has landed
+            } else {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+        }
+        return;
+    }
+
+    // ---- compute waves ---------------------------------------------------
+    const int grp = wave >> 1;    // row group
+    const int kh = wave & 1;      // key half: keys 64 kh .. 64 kh + 63
+    const int partner = wave ^ 1;
+    const int row = rb * CHUNK_ROWS + grp * 16 + l16;
+
+    // state x 16 (exact), accumulator layout: S4[b][r] = 16 S[row][64 kh + 16 b + 4 kk + r].
+    // With k and q also x16, every split operand and product stays well above
+    // the fp16 subnormal range; Lam carries the 1/256 back.
+    float *Srow = p.state + (((int64_t)n * hv + h) * 128 + row) * 128 + 64 * kh + 4 * kk;
+    f4 S4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b) * KQ_SCALE;
+
+    auto step = [&](int c) {
+        const int b = c & (NBUF - 1), x = c & 1;
         const int nv = min(CT, T_n - c * CT);
         const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
-        if (c + 1 < n_chunks) {
-            stage(std::integral_constant<int, b ^ 1>{});
-            if (c + 2 < n_chunks) fetch(c + 2);
-        }
-        const _Float16 *kh = reinterpret_cast<const _Float16 *>(sKH[b]);
+        const _Float16 *khp = reinterpret_cast<const _Float16 *>(sKH[b]);
         const float *vh = sVH[b];
-        // operands of this chunk
-        h8 kph[4], kpl[4], qph[4], qpl[4];
+        // operands of this chunk: K and Q for this wave's two 32-key steps
+        h8 kph[2], kpl[2], qph[2], qpl[2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            kph[s] = *reinterpret_cast<const h8 *>(kh + KH_KP + ((s * 2 + 0) * 64 + lane) * 8);
-            kpl[s] = *reinterpret_cast<const h8 *>(kh + KH_KP + ((s * 2 + 1) * 64 + lane) * 8);
-            qph[s] = *reinterpret_cast<const h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + lane) * 8);
-            qpl[s] = *reinterpret_cast<const h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + lane) * 8);
+        for (int i = 0; i < 2; ++i) {
+            const int s = 2 * kh + i;
+            kph[i] = *reinterpret_cast<const h8 *>(khp + KH_KP + ((s * 2 + 0) * 64 + lane) * 8);
+            kpl[i] = *reinterpret_cast<const h8 *>(khp + KH_KP + ((s * 2 + 1) * 64 + lane) * 8);
+            qph[i] = *reinterpret_cast<const h8 *>(khp + KH_QP + ((s * 2 + 0) * 64 + lane) * 8);
+            qpl[i] = *reinterpret_cast<const h8 *>(khp + KH_QP + ((s * 2 + 1) * 64 + lane) * 8);
         }
+        // partial P = K S^T and R = Q S^T (x256) over this wave's 64 keys
+        h8 sh[2], sl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) split8(S4[2 * i], S4[2 * i + 1], sh[i], sl[i], d.m1);
+        f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh, Rhh = Phh, Rhl = Phh, Rlh = Phh;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            Phh = mfma_k32(kph[i], sh[i], Phh);
+            Phl = mfma_k32(kph[i], sl[i], Phl);
+            Plh = mfma_k32(kpl[i], sh[i], Plh);
+        }
+        const f4 Pp = (Phh + Phl) + Plh;
+        sXP[x][wave][lane] = Pp;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            Rhh = mfma_k32(qph[i], sh[i], Rhh);
+            Rhl = mfma_k32(qph[i], sl[i], Rhl);
+            Rlh = mfma_k32(qpl[i], sh[i], Rlh);
+        }
+        const f4 Rp = (Rhh + Rhl) + Rlh;
+        if (kh == 1) sXR[x][grp][lane] = Rp;
+        lds_barrier();  // partials visible; every wave is past chunk c - 1
+
+        // the full P, summed in the same order by both waves of the pair
+        const f4 Po = sXP[x][partner][lane];
+        const f4 P = kh == 0 ? Pp + Po : Po + Pp;
         const h8 tp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_TP) + lane * 8);
-        const h8 mp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
         const f4 lam = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
         const f4 bet = *reinterpret_cast<const f4 *>(vh + VH_BETA + 4 * kk);
         const f4 wu = *reinterpret_cast<const f4 *>(vh + VH_W + 4 * kk);
         const float last = vh[VH_LAST];
-        const f4 vv = *reinterpret_cast<const f4 *>(&sV[b][wave * 16 + l16][4 * kk]);
-
-        // P = K S^T and R = Q S^T (x256): three split terms each, P first
-        // (it heads the chain to the next state), R behind it
-        h8 sh[4], sl[4];
+        f4 vv;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) split8(S4[2 * s], S4[2 * s + 1], sh[s], sl[s], d.m1);
-        f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh, Rhh = Phh, Rhl = Phh, Rlh = Phh;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            Phh = mfma_k32(kph[s], sh[s], Phh);
-            Phl = mfma_k32(kph[s], sl[s], Phl);
-            Plh = mfma_k32(kpl[s], sh[s], Plh);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            Rhh = mfma_k32(qph[s], sh[s], Rhh);
-            Rhl = mfma_k32(qph[s], sl[s], Rhl);
-            Rlh = mfma_k32(qpl[s], sh[s], Rlh);
-        }
-        const f4 P = (Phh + Phl) + Plh;
+        for (int r = 0; r < 4; ++r) vv[r] = sV[b][4 * kk + r][grp * 16 + l16];
         // B = beta (V - Lam P), component r is token 4 kk + r, channel l16
         f4 Bm;
 #pragma unroll
@@ -504,46 +552,40 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo
         const f4 z4 = {0.f, 0.f, 0.f, 0.f};
         const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4);
-        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): 8 key blocks
+        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks
         h4 uwh, uwl;
         split4(U * wu, uwh, uwl, d.m1);
         const h8 uww = cat(uwh, uwh);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const h8 kt = *reinterpret_cast<const h8 *>(kh + KH_KT + (kb * 64 + lane) * 8);
-            f4 C = S4[kb] * last;
+        for (int i = 0; i < 4; ++i) {
+            const h8 kt = *reinterpret_cast<const h8 *>(khp + KH_KT + ((4 * kh + i) * 64 + lane) * 8);
+            f4 C = S4[i] * last;
             C = mfma_k32(kt, uww, C);
             C = mfma_k16(lo_half(kt), uwl, C);
-            S4[kb] = C;
+            S4[i] = C;
         }
-        // O = (Lam R + M U) / sqrt(dk)
-        const f4 R = (Rhh + Rhl) + Rlh;
-        h4 uh, ul;
-        split4(U, uh, ul, d.m1);
-        f4 O = lam * R;
-        O = mfma_k32(mp, cat(uh, uh), O);
-        O = mfma_k16(lo_half(mp), ul, O);
-        char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + wave * 16);
+        // O = (Lam R + M U) / sqrt(dk), by the lower-key wave of the pair
+        if (kh == 0) {
+            const f4 R = Rp + sXR[x][grp][lane];
+            const h8 mp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
+            h4 uh, ul;
+            split4(U, uh, ul, d.m1);
+            f4 O = lam * R;
+            O = mfma_k32(mp, cat(uh, uh), O);
+            O = mfma_k16(lo_half(mp), ul, O);
+            char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + grp * 16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 4 * kk + r;
-            if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r] * SCALE;
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * kk + r;
+                if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r] * SCALE;
+            }
         }
-        __syncthreads();  // the chunk's buffers may be refilled after this
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    fetch(0);
-    stage(I0{});
-    if (n_chunks > 1) fetch(1);
-    __syncthreads();
-    for (int c = 0; c < n_chunks; c += 2) {
-        step(I0{}, c);
-        if (c + 1 < n_chunks) step(I1{}, c + 1);
-    }
+    lds_barrier();  // chunks 0 and 1 are in LDS
+    for (int c = 0; c < n_chunks; ++c) step(c);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) *reinterpret_cast<f4 *>(Srow + 16 * b) = S4[b] * (1.f / KQ_SCALE);
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f4 *>(Srow + 16 * i) = S4[i] * (1.f / KQ_SCALE);
 }
 
 static int64_t scan_slots(const gdn_shape &s)
