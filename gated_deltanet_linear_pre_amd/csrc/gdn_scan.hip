@@ -552,19 +552,22 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo
         const f4 z4 = {0.f, 0.f, 0.f, 0.f};
         const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4);
-        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks
         h4 uwh, uwl;
         split4(U * wu, uwh, uwl, d.m1);
         const h8 uww = cat(uwh, uwh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks,
+        // with the output of the lower-key wave of the pair,
+        // O = (Lam R + M U) / sqrt(dk), issued between them (off the chain to
+        // the next chunk)
+        auto update = [&](int i) {
             const h8 kt = *reinterpret_cast<const h8 *>(khp + KH_KT + ((4 * kh + i) * 64 + lane) * 8);
             f4 C = S4[i] * last;
             C = mfma_k32(kt, uww, C);
             C = mfma_k16(lo_half(kt), uwl, C);
             S4[i] = C;
-        }
-        // O = (Lam R + M U) / sqrt(dk), by the lower-key wave of the pair
+        };
+        update(0);
+        update(1);
         if (kh == 0) {
             const f4 R = Rp + sXR[x][grp][lane];
             const h8 mp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
@@ -573,13 +576,22 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
             f4 O = lam * R;
             O = mfma_k32(mp, cat(uh, uh), O);
             O = mfma_k16(lo_half(mp), ul, O);
+            O *= SCALE;
             char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + grp * 16);
+            if (nv == CT) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * kk + r;
-                if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r] * SCALE;
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<float *>(ob + ((uint32_t)(4 * kk + r) * vstride + l16) * 4u) = O[r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * kk + r;
+                    if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r];
+                }
             }
         }
+        update(2);
+        update(3);
     };
 
     lds_barrier();  // chunks 0 and 1 are in LDS
