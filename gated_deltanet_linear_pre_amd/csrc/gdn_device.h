@@ -29,6 +29,22 @@ __device__ __forceinline__ float row_sum16(float x)
     return x;
 }
 
+// ---- fast elementwise functions on the hardware transcendental unit -------
+// e^x = 2^(x log2 e) on v_exp_f32 (about 1 ulp of the power of two, plus the
+// rounding of x log2 e: relative error below 1e-6 for |x| < 40).
+__device__ __forceinline__ float exp_fast(float x)
+{
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+// x * sigmoid(x) = x / (1 + e^-x), with the v_rcp_f32 reciprocal (1 ulp).
+// For x -> -inf, e^-x overflows to inf and the result is x * 0 = -0.
+__device__ __forceinline__ float silu_fast(float x)
+{
+    return x * __builtin_amdgcn_rcpf(1.0f + exp_fast(-x));
+}
+// 1 / sqrt(x) on v_rsq_f32 (1 ulp).
+__device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
+
 // ---- 8 consecutive elements, widened to / narrowed from fp32 -------------
 
 __device__ __forceinline__ void load8(const float *__restrict__ p, float (&x)[8])

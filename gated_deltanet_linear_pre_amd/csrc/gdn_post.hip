@@ -38,12 +38,12 @@ __global__ __launch_bounds__(256) void post_kernel(const float *__restrict__ o,
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
     ss = row_sum16(ss);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+    const float inv = rsqrt_fast(ss * (1.0f / 128.0f) + eps);
 
     float out[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float gate = zz[i] / (1.0f + expf(-zz[i]));
+        const float gate = silu_fast(zz[i]);
         out[i] = ((x[i] * inv) * gm[i]) * gate;
     }
     store8(y + base, out);

@@ -128,11 +128,11 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
                 acc = fmaf(w[e][1], win[i + 1].get(e), acc);
                 acc = fmaf(w[e][2], win[i + 2].get(e), acc);
                 acc = fmaf(w[e][3], win[i + 3].get(e), acc);
-                s[e] = acc / (1.0f + expf(-acc));
+                s[e] = silu_fast(acc);
                 ss = fmaf(s[e], s[e], ss);
             }
             ss = row_sum16(ss);
-            const float sc = is_v ? 1.0f : 1.0f / sqrtf(ss + d.eps);
+            const float sc = is_v ? 1.0f : rsqrt_fast(ss + d.eps);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s[e] *= sc;
             if (active) store8(dst + (s0 + tau0 + i) * stride, s);
