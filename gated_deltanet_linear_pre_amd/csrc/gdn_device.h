@@ -90,25 +90,12 @@ template <> struct Raw8<_Float16> {
     __device__ __forceinline__ float get(int i) const { return (float)v[i]; }
 };
 template <> struct Raw8<float> {
-    float4 a, b;
-    __device__ __forceinline__ void load(const float *__restrict__ p)
-    {
-        a = reinterpret_cast<const float4 *>(p)[0];
-        b = reinterpret_cast<const float4 *>(p)[1];
-    }
-    __device__ __forceinline__ void store(float *__restrict__ p) const
-    {
-        reinterpret_cast<float4 *>(p)[0] = a;
-        reinterpret_cast<float4 *>(p)[1] = b;
-    }
-    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
-    __device__ __forceinline__ float get(int i) const
-    {
-        switch (i) {
-        case 0: return a.x; case 1: return a.y; case 2: return a.z; case 3: return a.w;
-        case 4: return b.x; case 5: return b.y; case 6: return b.z; default: return b.w;
-        }
-    }
+    typedef float f8 __attribute__((ext_vector_type(8), aligned(16)));
+    f8 v;
+    __device__ __forceinline__ void load(const float *__restrict__ p) { v = *reinterpret_cast<const f8 *>(p); }
+    __device__ __forceinline__ void store(float *__restrict__ p) const { *reinterpret_cast<f8 *>(p) = v; }
+    __device__ __forceinline__ void zero() { v = f8(0.f); }
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
 };
 
 } // namespace gdn
