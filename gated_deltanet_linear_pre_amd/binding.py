@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_workspace_bytes.argtypes = [SP]
         L.gdn_prefill_layer.restype = I
         L.gdn_prefill_layer.argtypes = [SP] + [P] * 13 + [S, P]
+        L.gdn_step.restype = I
+        L.gdn_step.argtypes = [SP] + [P] * 12
         _lib = L
     return _lib
 
@@ -159,4 +161,14 @@ def gdn_prefill_layer(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, z, g
         int(workspace_bytes), _stream(stream))
     if check:
         _check("gdn_prefill_layer", st)
+    return st
+
+
+def gdn_step(shape, qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist, state, y, stream=None,
+             check=True) -> int:
+    st = lib().gdn_step(ctypes.byref(shape), *map(_ptr, (qkv, conv_w, a, b, A_log, dt_bias, z,
+                                                            gamma, hist, state, y)),
+                        _stream(stream))
+    if check:
+        _check("gdn_step", st)
     return st

@@ -10,6 +10,7 @@ namespace {
 using gdn::PreArgs;
 using gdn::ScanArgs;
 using gdn::PostArgs;
+using gdn::StepArgs;
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;
 constexpr int kMaxHeads = 1 << 12;
@@ -209,6 +210,22 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     if (gdn::launch_scan(*shape, sa, s) != hipSuccess) return GDN_E_LAUNCH;
     const PostArgs po{o, z, gamma, y};
     return launch_status(gdn::launch_post(*shape, po, s));
+}
+
+int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w, const void *a,
+             const void *b, const void *A_log, const void *dt_bias, const void *z,
+             const void *gamma, void *hist, float *state, void *y, void *stream)
+{
+    int st = check_shape(shape);
+    if (st) return st;
+    if (shape->total_T != shape->n_seq || shape->max_T != 1) return GDN_E_SHAPE;
+    REQ(qkv); REQ(conv_w); REQ(a); REQ(b); REQ(A_log); REQ(dt_bias); REQ(z); REQ(gamma);
+    REQ(hist); REQ(state); REQ(y);
+    ALN(a, 4); ALN(b, 4); ALN(A_log, 4); ALN(dt_bias, 4);
+    ALN(qkv, 16); ALN(conv_w, 16); ALN(z, 16); ALN(gamma, 16); ALN(hist, 16); ALN(state, 16);
+    ALN(y, 16);
+    const StepArgs sa{qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist, state, y};
+    return launch_status(gdn::launch_step(*shape, sa, (hipStream_t)stream));
 }
 
 } // extern "C"

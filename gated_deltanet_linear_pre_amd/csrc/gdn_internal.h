@@ -36,9 +36,17 @@ struct PostArgs {
     void *y;
 };
 
+struct StepArgs {
+    const void *qkv, *conv_w, *a, *b, *A_log, *dt_bias, *z, *gamma;
+    void *hist;
+    float *state;
+    void *y;
+};
+
 hipError_t launch_pre(const gdn_shape &s, const PreArgs &a, hipStream_t st);
 hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st);
 hipError_t launch_post(const gdn_shape &s, const PostArgs &a, hipStream_t st);
+hipError_t launch_step(const gdn_shape &s, const StepArgs &a, hipStream_t st);
 
 // Grid-size limits the ABI checks before launching.
 constexpr int PRE_TILE_F16 = 16;  // tokens per pre tile, fp16 storage

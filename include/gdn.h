@@ -10,6 +10,7 @@
  *   gdn_post  per-(token, value head) RMSNorm with gamma, times SiLU(z).
  *   gdn_prefill_layer  pre -> scan -> post with the intermediates in a
  *             caller-provided workspace.
+ *   gdn_step  one decode token per sequence through the whole layer.
  *
  * The stage split, the buffer set (q, k, v, gates, history, o, state, y)
  * and the fp16/fp32 output switch are those of the audited Metal path:
@@ -69,7 +70,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -195,6 +196,33 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens,
                       const void *z, const void *gamma, void *hist,
                       float *state, void *y, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_step -- one decode token for each of n_seq sequences through the whole
+ * layer.  "Round 30 Track C Audit", section 1 (gdn_scan_r findings): the
+ * single-token update of the per-value-head state, the step every scan
+ * variant is checked against; section 2: running T steps must agree with
+ * one T-token pass.
+ *
+ * shape->total_T must equal shape->n_seq and shape->max_T must be 1: token
+ * row n of qkv, a, b, z and y belongs to sequence n (no cu_seqlens).  Per
+ * sequence n the arithmetic is that of gdn_pre, gdn_scan and gdn_post for
+ * one token, with the same layouts:
+ *   X = [hist[n]; qkv[n]] (4 x C), x~[c] = sum_m conv_w[c][m] X[m][c],
+ *   s = SiLU(x~), qn/kn the L2-normalised key-head blocks, v the value block;
+ *   alpha = exp(g), g and beta as in gdn_pre;
+ *   S <- alpha*S + beta (v - alpha*S kn) kn^T,  o = S qn / sqrt(dk)  (fp32)
+ *   y = o / sqrt(mean(o^2) + eps_rms) * gamma * z * sigmoid(z)  -> out_dtype
+ *   hist[n] <- X[1..3]
+ * In:  qkv [n_seq][C], conv_w, a, b [n_seq][hv], A_log, dt_bias, z
+ *      [n_seq][hv][dv], gamma; hist and state (read).
+ * Out: y [n_seq][hv][dv]; hist and state (overwritten in place).
+ * No workspace.  Two kernels are enqueued (the step, then the history shift).
+ */
+int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w,
+             const void *a, const void *b, const void *A_log,
+             const void *dt_bias, const void *z, const void *gamma, void *hist,
+             float *state, void *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,13 +26,13 @@ def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_pre", "gdn_scan",
                           "gdn_scan_workspace_bytes", "gdn_post", "gdn_prefill_workspace_bytes",
-                          "gdn_prefill_layer"}
+                          "gdn_prefill_layer", "gdn_step"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert B.gdn_abi_version() == 2
+    assert B.gdn_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert B.gdn_status_str(code) and B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(-99) == "unknown status"
@@ -162,3 +162,35 @@ def test_zero_tokens_is_a_noop_that_succeeds():
     assert _scan(s, o=None, ws=None, ws_bytes=0) == 0
     assert _post(s, y=None) == 0
     assert _layer(s, ws=None, ws_bytes=0) == 0
+
+
+def _step(s, **over):
+    args = dict(qkv=P, conv_w=P, a=P, b=P, A_log=P, dt_bias=P, z=P, gamma=P, hist=P, state=P, y=P)
+    args.update(over)
+    return B.gdn_step(s, *args.values(), stream=0, check=False)
+
+
+def step_shape(**kw):
+    d = dict(n_seq=4, total_T=4, max_T=1)
+    d.update(kw)
+    return shape(**d)
+
+
+def test_step_shape_rules():
+    # one token per sequence: total_T == n_seq and max_T == 1
+    assert _step(step_shape(total_T=5, max_T=2)) == -2
+    assert _step(step_shape(total_T=4, max_T=2)) == -2
+    assert _step(step_shape(total_T=3)) == -2
+    assert _step(step_shape(total_T=0, max_T=0)) == -2
+    for over, code in BAD_SHAPES:
+        if "n_seq" in over or "total_T" in over or "max_T" in over:
+            continue
+        assert _step(step_shape(**over)) == code
+
+
+@pytest.mark.parametrize("name", ["qkv", "conv_w", "a", "b", "A_log", "dt_bias", "z", "gamma",
+                                  "hist", "state", "y"])
+def test_step_null_and_alignment(name):
+    assert _step(step_shape(), **{name: None}) == -1
+    assert _step(step_shape(), **{name: P + 2}) == -3
+

@@ -1,0 +1,106 @@
+"""gdn_step (one decode token per sequence through the whole layer) against
+the fp64 oracle, and against the prefill path.
+
+"Round 30 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 1: the
+single-token step is what every scan variant is checked against; section 2:
+T steps must agree with one T-token pass.  The oracle runs the same layer with
+one token per sequence (cu_seqlens = 0, 1, 2, ...), so no oracle code is
+specific to the step.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_pre_amd import binding as B
+from gated_deltanet_linear_pre_amd import synth
+from gated_deltanet_linear_pre_amd.buffers import LayerBuffers
+from oracle import gdn_oracle as orc
+
+from . import parity
+from .gpu_util import Guarded, banner, np_
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(buf, y=None, state=None, hist=None):
+    B.gdn_step(buf.shape, buf.qkv, buf.conv_w, buf.a, buf.b, buf.A_log, buf.dt_bias, buf.z,
+               buf.gamma, buf.hist if hist is None else hist,
+               buf.state if state is None else state, buf.y if y is None else y)
+
+
+CASES = [
+    # name, hk, hv, n_seq, io, out
+    ("prod_batch5_fp16", 16, 48, 5, "f16", "f16"),
+    ("prod_batch3_fp16in_fp32out", 16, 48, 3, "f16", "f32"),
+    ("tiny_batch4_fp32", 2, 6, 4, "f32", "f32"),
+    ("tiny_batch1_fp32in_fp16out", 2, 6, 1, "f32", "f16"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_step_matches_oracle(gpu, case):
+    name, hk, hv, n, io, out = case
+    w = synth.Workload(name, hk=hk, hv=hv, seqlens=(1,) * n, io=io, out=out, seed=(31, n),
+                       s0_std=0.05, hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    buf = LayerBuffers.create(w, inp)
+    y = Guarded(tuple(buf.y.shape), buf.y.dtype)
+    state = Guarded(tuple(buf.state.shape), torch.float32, init=buf.state)
+    hist = Guarded(tuple(buf.hist.shape), buf.hist.dtype, init=buf.hist)
+    banner("gdn_step", name, f"n_seq={n}")
+    _step(buf, y=y.t, state=state.t, hist=hist.t)
+    torch.cuda.synchronize()
+    assert y.intact() and state.intact() and hist.intact()
+    ref = orc.layer(orc.Dims(hk, hv), w.cu_seqlens(), inp)
+    parity.check_y(np_(y.t).reshape(n, hv, 128), ref["y"], out)
+    parity.check_state(np_(state.t), ref["S"])
+    parity.check_exact("hist", np_(hist.t).astype(np.float64), ref["hist"])
+
+
+def test_steps_match_prefill_and_oracle(gpu):
+    # 37 decode steps of one sequence vs one 37-token prefill call: both
+    # against the oracle, and against each other within the same bars
+    T = 37
+    w = synth.Workload("steps_vs_prefill", hk=16, hv=48, seqlens=(T,), seed=(32,), s0_std=0.05,
+                       hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    ref = orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp)
+    banner("gdn_prefill_layer", w.name, f"T={T}")
+    pre = LayerBuffers.create(w, inp)
+    ws = pre.workspace()
+    pre.run_layer(ws)
+    torch.cuda.synchronize()
+    one = synth.Workload("steps_vs_prefill_1", hk=16, hv=48, seqlens=(1,), seed=(32,))
+    hist, state = inp["hist"], inp["S0"]
+    ys = []
+    for t in range(T):
+        part = dict(inp, hist=hist, S0=state)
+        for k in ("qkv", "a", "b", "z"):
+            part[k] = inp[k][t:t + 1]
+        banner("gdn_step", w.name, f"token {t}")
+        buf = LayerBuffers.create(one, part)
+        _step(buf)
+        torch.cuda.synchronize()
+        ys.append(np_(buf.y))
+        hist, state = np_(buf.hist), np_(buf.state)
+    y = np.concatenate(ys).reshape(T, w.hv, 128)
+    parity.check_y(y, ref["y"], "f16", what="y (steps)")
+    parity.check_state(state, ref["S"])
+    parity.check_exact("hist (steps)", hist.astype(np.float64), ref["hist"])
+    parity.check_y(np_(pre.y).reshape(T, w.hv, 128), ref["y"], "f16", what="y (prefill)")
+    parity.check_state(state, np_(pre.state).astype(np.float64))
+    assert np.array_equal(hist.view(np.uint16), np_(pre.hist).view(np.uint16))
+
+
+def test_step_is_bitwise_deterministic(gpu):
+    w = synth.Workload("step_det", hk=16, hv=48, seqlens=(1,) * 8, seed=(33,), s0_std=0.05,
+                       hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    outs = []
+    for _ in range(2):
+        buf = LayerBuffers.create(w, inp)
+        banner("gdn_step", w.name)
+        _step(buf)
+        torch.cuda.synchronize()
+        outs.append((np_(buf.y).view(np.uint16), np_(buf.state).view(np.uint32)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
