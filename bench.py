@@ -226,6 +226,42 @@ def main():
             "scan_tflops": round(scan_flops(T, hv) / (r["scan_ms"] / 1e3) / 1e12, 3),
         }
 
+    def decode(batch, layers=36, steps=20):
+        # gdn_step over `layers` layers, each with its own weights, state and
+        # history (distinct buffers), one token per sequence per step
+        wd = synth.Workload(f"decode_b{batch}", hk=hk, hv=hv, seqlens=(1,) * batch, seed=(41,),
+                            s0_std=0.05, hist_std=1.0)
+        shape = B.make_shape(hk, hv, batch, batch, 1, io="f16", out="f16")
+        ls = []
+        for l in range(layers):
+            inp = synth.layer_inputs(wd, l)
+            ls.append({k: upload(v, dev) for k, v in inp.items()})
+        y = torch.empty((batch, hv * 128), dtype=torch.float16, device=dev)
+
+        def one():
+            for d in ls:
+                B.gdn_step(shape, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                           d["z"], d["gamma"], d["hist"], d["S0"], y, stream=stream)
+        for _ in range(3):
+            one()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            one()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+        C = 2 * hk * 128 + hv * 128
+        byts = batch * (2 * hv * 128 * 128 * 4 + C * 2 + 4 * 3 * C * 2 + 2 * hv * 2 + 2 * hv * 128 * 2)
+        return {"batch": batch, "us_per_layer": round(us, 2),
+                "tokens_per_s": round(batch / (us * 1e-6 * layers), 1),
+                "bytes_per_layer": byts, "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    log("timing gdn_step decode")
+    dec = [decode(b) for b in (1, 8, 64)]
+
     res = {
         "metric": METRIC,
         "value": round(T / (r16["ms_per_step"] / 1e3), 1),
@@ -246,6 +282,7 @@ def main():
         "stages_fp16_out": stage_report(r16, 2),
         "fp32_out": {"value": round(T / (r32["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
                      "ms_per_step": round(r32["ms_per_step"], 4), **stage_report(r32, 4)},
+        "decode_gdn_step": dec,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
