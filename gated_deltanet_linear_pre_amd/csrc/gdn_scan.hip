@@ -188,10 +188,10 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 {
     __shared__ __attribute__((aligned(16))) float sK[CT][KS];
     __shared__ __attribute__((aligned(16))) float sQ[CT][KS];
-    __shared__ float sKK[CT][CT + 1];
-    __shared__ float sQK[CT][CT + 1];
+    __shared__ __attribute__((aligned(16))) f4 sPart[2][4][64];  // per-wave partial K K^T, K Q^T
     __shared__ float sA[4][CT][CT + 1];
     __shared__ float sTm[4][CT][CT + 1];
+    __shared__ __attribute__((aligned(16))) float sGB[4][2][CT];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -207,6 +207,16 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
     const int hk = d.hk, hv = d.hv;
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
     const int64_t slot = chunk_slot(cu0, n, c);
+
+    // g and beta of this wave's first value head, lane t % 16 holding token t
+    // (requested first, so their latency overlaps the staging below)
+    auto load_gb = [&](int gh, float &gl, float &bl) {
+        const int64_t e = (tb + min(l16, nv - 1)) * hv + j * d.G + gh;
+        gl = l16 < nv ? p.g[e] : 0.f;
+        bl = l16 < nv ? p.beta[e] : 0.f;
+    };
+    float g_next = 0.f, b_next = 0.f;
+    if (wave < d.G) load_gb(wave, g_next, b_next);
 
     // stage the chunk's k and q rows of key head j (zero past the end)
 #pragma unroll
@@ -235,13 +245,17 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
             qa[e] = KQ_SCALE * sQ[t][32 * s + 4 * kk + e];
             qb[e] = KQ_SCALE * sQ[t][32 * s + 16 + 4 * kk + e];
         }
-        h8 hi, lo;
-        split8(ka, kb, hi, lo, d.m1);
-        *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 0) * 64 + L) * 8) = hi;
-        *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 1) * 64 + L) * 8) = lo;
-        split8(qa, qb, hi, lo, d.m1);
-        *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + L) * 8) = hi;
-        *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + L) * 8) = lo;
+        h8 khi, klo, qhi, qlo;
+        split8(ka, kb, khi, klo, d.m1);
+        *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 0) * 64 + L) * 8) = khi;
+        *reinterpret_cast<h8 *>(kh + KH_KP + ((s * 2 + 1) * 64 + L) * 8) = klo;
+        split8(qa, qb, qhi, qlo, d.m1);
+        *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 0) * 64 + L) * 8) = qhi;
+        *reinterpret_cast<h8 *>(kh + KH_QP + ((s * 2 + 1) * 64 + L) * 8) = qlo;
+        // this wave's 32 keys of K K^T and K Q^T (x256) from the same split
+        // operands: as A and as B operand, lane (t, kk) holds the same K[t][keys]
+        sPart[0][wave][lane] = (mfma_k32(khi, khi, z4) + mfma_k32(khi, klo, z4)) + mfma_k32(klo, khi, z4);
+        sPart[1][wave][lane] = (mfma_k32(khi, qhi, z4) + mfma_k32(khi, qlo, z4)) + mfma_k32(klo, qhi, z4);
         // K^T block b, lane L = 16 kk + m holds K[4 kk + e][16 b + m]
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2) {
@@ -255,59 +269,71 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
         }
     }
 
-    // wave 0: K K^T, wave 1: Q K^T (16 x 16 over 128 keys, fp32 MFMA)
-    if (wave < 2) {
-        const float(*X)[KS] = wave == 0 ? sK : sQ;
-        f4 acc = z4;
-#pragma unroll
-        for (int jb = 0; jb < 8; ++jb) {
-            const f4 xa = *reinterpret_cast<const f4 *>(&X[l16][16 * jb + 4 * kk]);
-            const f4 kb = *reinterpret_cast<const f4 *>(&sK[l16][16 * jb + 4 * kk]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc = mfma_f32(xa[r], kb[r], acc);
-        }
-        float(*O)[CT + 1] = wave == 0 ? sKK : sQK;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O[4 * kk + r][l16] = acc[r];
-    }
     __syncthreads();
+    // k_t.k_u and k_t.q_u summed over the four key steps in one order by every
+    // wave; lane (u = l16, kk) holds component r = (t - 4 kk): KK4[r] =
+    // k_{4 kk + r}.k_{l16} and KQ4[r] = k_{4 kk + r}.q_{l16}
+    f4 KK4, KQ4;
+    {
+        const float unscale = 1.f / (KQ_SCALE * KQ_SCALE);
+        KK4 = (((sPart[0][0][lane] + sPart[0][1][lane]) + sPart[0][2][lane]) + sPart[0][3][lane]) * unscale;
+        KQ4 = (((sPart[1][0][lane] + sPart[1][1][lane]) + sPart[1][2][lane]) + sPart[1][3][lane]) * unscale;
+    }
 
     // ---- value-head slots ------------------------------------------------
     for (int gh = wave; gh < d.G; gh += 4) {
         const int h = j * d.G + gh;
         float *vs = p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS;
-        float gv[CT], bv[CT];
-#pragma unroll
-        for (int t = 0; t < CT; ++t) {
-            const int tc = min(t, nv - 1);
-            const float gg = p.g[(tb + tc) * hv + h];
-            const float bb = p.beta[(tb + tc) * hv + h];
-            gv[t] = t < nv ? gg : 0.f;
-            bv[t] = t < nv ? bb : 0.f;
+        // the head's 16 g and beta, uniform across the wave (0 past the end)
+        const float g_own = g_next, b_own = b_next;
+        if (gh + 4 < d.G) load_gb(gh + 4, g_next, b_next);
+        // the 16 g and beta through this wave's LDS row: every lane reads the
+        // g row as uniform VGPRs, and its own 4-token pieces of g and beta
+        if (lane < CT) {
+            sGB[wave][0][lane] = g_own;
+            sGB[wave][1][lane] = b_own;
         }
-        // A (to LDS) by entries e = lane + 64 m
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float gv[CT];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = lane + 64 * m;
-            const int t = e >> 4, s = e & 15;
-            float sum = 0.f;
-#pragma unroll
-            for (int r = 1; r < CT; ++r)
-                if (r > s && r <= t) sum += gv[r];
-            sA[wave][t][s] = (t < nv && s < t) ? bv[t] * expf(sum) * sKK[t][s] : 0.f;
+        for (int i = 0; i < CT / 4; ++i) {
+            const f4 x = *reinterpret_cast<const f4 *>(&sGB[wave][0][4 * i]);
+            gv[4 * i] = x[0]; gv[4 * i + 1] = x[1]; gv[4 * i + 2] = x[2]; gv[4 * i + 3] = x[3];
         }
-        // M in operand order: lane L = 16 kk + t holds M[t][4 kk + e]
+        const f4 g4 = *reinterpret_cast<const f4 *>(&sGB[wave][0][4 * kk]);  // g[4 kk + i]
+        const f4 b4 = *reinterpret_cast<const f4 *>(&sGB[wave][1][4 * kk]);  // beta[4 kk + i]
+        // Every decay is the exp of a direct sum of the log decays it spans.
+        // A[t][s] = beta_t D[t][s] k_t.k_s (s < t): lane (s = l16, kk) takes
+        // t = 4 kk .. 4 kk + 3, summing g over (s, 4 kk] once and then one
+        // term per t.
+        {
+            const int s0 = l16;
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 1; r < CT; ++r) acc += (r > s0 && r <= 4 * kk) ? gv[r] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * kk + i;
+                if (i > 0) acc += t > s0 ? g4[i] : 0.f;
+                sA[wave][t][s0] = (t < nv && s0 < t) ? b4[i] * exp_fast(acc) * KK4[i] : 0.f;
+            }
+        }
+        // M[t][s] = D[t][s] q_t.k_s (s <= t) in operand order: lane L = 16 kk + t
+        // holds s = 4 kk + e; the sum over (4 kk + 3, t] first, then one term
+        // per step down in s
         {
             const int t = l16;
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 1; r < CT; ++r) acc += (r >= 4 * kk + 4 && r <= t) ? gv[r] : 0.f;
             f4 mv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = 4 * kk + e;
-                float sum = 0.f;
-#pragma unroll
-                for (int r = 1; r < CT; ++r)
-                    if (r > s && r <= t) sum += gv[r];
-                mv[e] = (t < nv && s <= t) ? expf(sum) * sQK[t][s] : 0.f;
+            for (int e = 3; e >= 0; --e) {
+                const int s0 = 4 * kk + e;
+                if (e < 3) acc += (s0 + 1 <= t) ? g4[e + 1] : 0.f;
+                mv[e] = (t < nv && s0 <= t) ? exp_fast(acc) * KQ4[e] : 0.f;
             }
             h4 hi, lo;
             split4(mv, hi, lo, d.m1);
@@ -318,14 +344,16 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
             float lam = 0.f, wdec = 0.f;
 #pragma unroll
             for (int r = 0; r < CT; ++r) {
-                if (r <= t) lam += gv[r];
-                if (r > t && r < nv) wdec += gv[r];
+                lam += r <= t ? gv[r] : 0.f;
+                wdec += (r > t && r < nv) ? gv[r] : 0.f;
             }
-            const float L = t < nv ? expf(lam) : 0.f;
-            vs[VH_LAM + t] = L * (1.f / (KQ_SCALE * KQ_SCALE));
-            vs[VH_BETA + t] = bv[t];
-            vs[VH_W + t] = t < nv ? expf(wdec) : 0.f;
-            if (t == nv - 1) vs[VH_LAST] = L;
+            // Lam_t and D[last][t] weight this chunk's terms only; Lam_last
+            // multiplies the whole state every chunk, so it takes the
+            // correctly rounded exp
+            vs[VH_LAM + t] = t < nv ? exp_fast(lam) * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
+            vs[VH_BETA + t] = b_own;
+            vs[VH_W + t] = t < nv ? exp_fast(wdec) : 0.f;
+            if (t == nv - 1) vs[VH_LAST] = expf(lam);
         }
         // the wave's A writes must land before its lanes read them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -337,10 +365,11 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
             float Tc[CT];
 #pragma unroll
             for (int t = 0; t < CT; ++t) {
-                float acc = (t == s) ? 1.f : 0.f;
+                // four interleaved partial sums shorten the dependent chain
+                float acc[4] = {(t == s) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < t; ++r) acc = fmaf(-sA[wave][t][r], Tc[r], acc);
-                Tc[t] = acc;
+                for (int r = 0; r < t; ++r) acc[r & 3] = fmaf(-sA[wave][t][r], Tc[r], acc[r & 3]);
+                Tc[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
 #pragma unroll
             for (int t = 0; t < CT; ++t) sTm[wave][t][s] = Tc[t];
