@@ -204,10 +204,16 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     st = check_post(o, z, gamma, y);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    const PreArgs pa{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta};
-    if (gdn::launch_pre(*shape, pa, s) != hipSuccess) return GDN_E_LAUNCH;
     const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o, sws};
-    if (gdn::launch_scan(*shape, sa, s) != hipSuccess) return GDN_E_LAUNCH;
+    if (shape->hv / shape->hk <= gdn::LAYER_G_MAX) {
+        // pre fused into the scan's prep step: q, k and the gates stay on chip
+        const gdn::LayerPrepArgs lp{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, vc, sws};
+        if (gdn::launch_layer_scan(*shape, lp, sa, s) != hipSuccess) return GDN_E_LAUNCH;
+    } else {
+        const PreArgs pa{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta};
+        if (gdn::launch_pre(*shape, pa, s) != hipSuccess) return GDN_E_LAUNCH;
+        if (gdn::launch_scan(*shape, sa, s) != hipSuccess) return GDN_E_LAUNCH;
+    }
     const PostArgs po{o, z, gamma, y};
     return launch_status(gdn::launch_post(*shape, po, s));
 }

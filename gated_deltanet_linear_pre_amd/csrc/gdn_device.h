@@ -45,6 +45,29 @@ __device__ __forceinline__ float silu_fast(float x)
 // 1 / sqrt(x) on v_rsq_f32 (1 ulp).
 __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// ---- per-element arithmetic of the pre stage, shared by every kernel that
+// runs it (one expression, so the compiler rounds it the same way everywhere)
+// 4-tap conv of one channel: taps in order, tap 3 on the current token
+__device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, float x0, float x1,
+                                       float x2, float x3)
+{
+    float acc = w0 * x0;
+    acc = fmaf(w1, x1, acc);
+    acc = fmaf(w2, x2, acc);
+    acc = fmaf(w3, x3, acc);
+    return acc;
+}
+// g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b), on the libm
+// exp/log1p (these feed every decay of the scan)
+__device__ __forceinline__ void gates(float a, float dt_bias, float A_log, float b, float &g,
+                                      float &beta)
+{
+    const float x = a + dt_bias;
+    const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    g = -expf(A_log) * sp;
+    beta = 1.0f / (1.0f + expf(-b));
+}
+
 // ---- 8 consecutive elements, widened to / narrowed from fp32 -------------
 
 __device__ __forceinline__ void load8(const float *__restrict__ p, float (&x)[8])

@@ -30,6 +30,17 @@ constexpr int SCAN_KH_FLOATS = 6144;
 constexpr int SCAN_SLOT_FLOATS = 576;
 size_t scan_workspace_bytes(const gdn_shape &s);
 
+// The layer path's fused pre + prep step: the pre-stage inputs, the history
+// (in/out), and the two buffers the chunk kernel reads (vc and the slots).
+struct LayerPrepArgs {
+    const int32_t *cu;
+    const void *qkv, *conv_w, *a, *b, *A_log, *dt_bias;
+    void *hist;
+    float *vc;
+    float *ws;
+};
+constexpr int LAYER_G_MAX = 8;  // value heads per key head the fused step handles
+
 struct PostArgs {
     const float *o;
     const void *z, *gamma;
@@ -45,6 +56,8 @@ struct StepArgs {
 
 hipError_t launch_pre(const gdn_shape &s, const PreArgs &a, hipStream_t st);
 hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st);
+hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const ScanArgs &a,
+                             hipStream_t st);
 hipError_t launch_post(const gdn_shape &s, const PostArgs &a, hipStream_t st);
 hipError_t launch_step(const gdn_shape &s, const StepArgs &a, hipStream_t st);
 

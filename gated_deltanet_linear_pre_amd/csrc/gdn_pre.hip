@@ -65,10 +65,7 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
             const int i = idx / hv;
             const int h = idx - i * hv;
             const int64_t e = (s0 + tau0 + i) * hv + h;
-            const float x = ld1(a + e) + ld1(dt_bias + h);
-            const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-            p.g[e] = -expf(ld1(A_log + h)) * sp;
-            p.beta[e] = 1.0f / (1.0f + expf(-ld1(b + e)));
+            gates(ld1(a + e), ld1(dt_bias + h), ld1(A_log + h), ld1(b + e), p.g[e], p.beta[e]);
         }
         return;
     }
@@ -124,10 +121,8 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float acc = w[e][0] * win[i].get(e);
-                acc = fmaf(w[e][1], win[i + 1].get(e), acc);
-                acc = fmaf(w[e][2], win[i + 2].get(e), acc);
-                acc = fmaf(w[e][3], win[i + 3].get(e), acc);
+                const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], win[i].get(e),
+                                        win[i + 1].get(e), win[i + 2].get(e), win[i + 3].get(e));
                 s[e] = silu_fast(acc);
                 ss = fmaf(s[e], s[e], ss);
             }

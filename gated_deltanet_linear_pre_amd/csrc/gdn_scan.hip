@@ -182,55 +182,43 @@ struct PrepDims {
     int hk, hv, G, n_chunk_max;
     float m1;         // -1 (see lo_pair)
     int64_t vh_base;  // float offset of the value-head slots in the workspace
+    int C;            // channels of a qkv row (fused layer prep)
+    float eps_l2;     // (fused layer prep)
 };
 
-__global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
-{
-    __shared__ __attribute__((aligned(16))) float sK[CT][KS];
-    __shared__ __attribute__((aligned(16))) float sQ[CT][KS];
-    __shared__ __attribute__((aligned(16))) f4 sPart[2][4][64];  // per-wave partial K K^T, K Q^T
-    __shared__ float sA[4][CT][CT + 1];
-    __shared__ float sTm[4][CT][CT + 1];
-    __shared__ __attribute__((aligned(16))) float sGB[4][2][CT];
+// LDS of the prep step of one (chunk, key head)
+struct PrepShared {
+    float sK[CT][KS];           // k and q of the chunk (zero past the end)
+    float sQ[CT][KS];
+    f4 sPart[2][4][64];         // per-wave partial K K^T, K Q^T
+    float sA[4][CT][CT + 1];
+    float sTm[4][CT][CT + 1];
+    float sGB[4][2][CT];
+};
 
+// Everything after k and q of the chunk are in LDS: the key-head slot and the
+// value-head slots.  load_gb(gh, g, b) gives lane t % 16 the g and beta of
+// token t of value head gh of the group (0 past the end); g_next, b_next
+// already hold those of this wave's first head.
+template <class GB>
+__device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepDims &d, int j,
+                                          int64_t slot, int nv, float g_next, float b_next,
+                                          GB load_gb)
+{
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
-    const int n = blockIdx.x / d.n_chunk_max;
-    const int c = blockIdx.x - n * d.n_chunk_max;
-    const int j = blockIdx.y;
-    const int cu0 = p.cu[n];
-    const int T_n = p.cu[n + 1] - cu0;
-    if (c * CT >= T_n) return;
-    const int nv = min(CT, T_n - c * CT);
-    const int64_t tb = (int64_t)cu0 + c * CT;
     const int hk = d.hk, hv = d.hv;
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
-    const int64_t slot = chunk_slot(cu0, n, c);
-
-    // g and beta of this wave's first value head, lane t % 16 holding token t
-    // (requested first, so their latency overlaps the staging below)
-    auto load_gb = [&](int gh, float &gl, float &bl) {
-        const int64_t e = (tb + min(l16, nv - 1)) * hv + j * d.G + gh;
-        gl = l16 < nv ? p.g[e] : 0.f;
-        bl = l16 < nv ? p.beta[e] : 0.f;
-    };
-    float g_next = 0.f, b_next = 0.f;
-    if (wave < d.G) load_gb(wave, g_next, b_next);
-
-    // stage the chunk's k and q rows of key head j (zero past the end)
-#pragma unroll
-    for (int f2 = 0; f2 < 2; ++f2) {
-        const int f = tid + 256 * f2;
-        const int t = f >> 5, col = (f & 31) * 4;
-        const int tc = min(t, nv - 1);
-        const int64_t off = ((tb + tc) * hk + j) * 128 + col;
-        const f4 kv = *reinterpret_cast<const f4 *>(p.kn + off);
-        const f4 qv = *reinterpret_cast<const f4 *>(p.qn + off);
-        *reinterpret_cast<f4 *>(&sK[t][col]) = t < nv ? kv : z4;
-        *reinterpret_cast<f4 *>(&sQ[t][col]) = t < nv ? qv : z4;
-    }
-    __syncthreads();
+    auto &sK = sm.sK;
+    auto &sQ = sm.sQ;
+    auto &sPart = sm.sPart;
+    auto &sA = sm.sA;
+    auto &sTm = sm.sTm;
+    auto &sGB = sm.sGB;
+    struct {
+        float *ws;
+    } p{ws};
 
     // ---- key-head slot: K, Q and K^T split and packed in operand order ----
     _Float16 *kh = reinterpret_cast<_Float16 *>(p.ws + (slot * hk + j) * SCAN_KH_FLOATS);
@@ -388,6 +376,51 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
         }
         __builtin_amdgcn_wave_barrier();
     }
+}
+
+constexpr int CHUNK_PREP_THREADS = 256;
+
+__global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
+{
+    __shared__ __attribute__((aligned(16))) PrepShared sm;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15;
+    const int n = blockIdx.x / d.n_chunk_max;
+    const int c = blockIdx.x - n * d.n_chunk_max;
+    const int j = blockIdx.y;
+    const int cu0 = p.cu[n];
+    const int T_n = p.cu[n + 1] - cu0;
+    if (c * CT >= T_n) return;
+    const int nv = min(CT, T_n - c * CT);
+    const int64_t tb = (int64_t)cu0 + c * CT;
+    const int hk = d.hk, hv = d.hv;
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+    // g and beta of this wave's first value head, lane t % 16 holding token t
+    // (requested first, so their latency overlaps the staging below)
+    auto load_gb = [&](int gh, float &gl, float &bl) {
+        const int64_t e = (tb + min(l16, nv - 1)) * hv + j * d.G + gh;
+        gl = l16 < nv ? p.g[e] : 0.f;
+        bl = l16 < nv ? p.beta[e] : 0.f;
+    };
+    float g_next = 0.f, b_next = 0.f;
+    if (wave < d.G) load_gb(wave, g_next, b_next);
+
+    // stage the chunk's k and q rows of key head j (zero past the end)
+#pragma unroll
+    for (int f2 = 0; f2 < 2; ++f2) {
+        const int f = tid + 256 * f2;
+        const int t = f >> 5, col = (f & 31) * 4;
+        const int tc = min(t, nv - 1);
+        const int64_t off = ((tb + tc) * hk + j) * 128 + col;
+        const f4 kv = *reinterpret_cast<const f4 *>(p.kn + off);
+        const f4 qv = *reinterpret_cast<const f4 *>(p.qn + off);
+        *reinterpret_cast<f4 *>(&sm.sK[t][col]) = t < nv ? kv : z4;
+        *reinterpret_cast<f4 *>(&sm.sQ[t][col]) = t < nv ? qv : z4;
+    }
+    __syncthreads();
+    prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c), nv, g_next, b_next, load_gb);
 }
 
 struct ChunkDims {
@@ -634,29 +667,180 @@ static int64_t scan_slots(const gdn_shape &s)
     return s.total_T / CT + (int64_t)s.n_seq + 1;
 }
 
-hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
+// ---- the layer's pre stage fused into the prep step ------------------------
+//
+// One block per (chunk, key head j) computes, for the chunk's 16 tokens, the
+// pre stage of exactly the channels the prep step needs: q and k of key head
+// j (conv, SiLU, L2 norm) straight into LDS, v of the group's value heads
+// (conv, SiLU) to the vc buffer the chunk kernel reads, and the group's
+// gates; then it builds the slots like scan_prep_kernel.  The normalised q
+// and k and the gates never go through memory.  The arithmetic is that of
+// gdn_pre (the same per-element expressions), so the layer's results equal
+// the staged path's bit for bit.  History carry without a race: only the
+// chunk-0 blocks read the old history, each for its own channels, and the
+// same block writes the new history of those channels after a barrier.
+template <typename TI>
+__global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDims d)
 {
-    const int64_t vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
+    __shared__ __attribute__((aligned(16))) PrepShared sm;
+    __shared__ float sGate[LAYER_G_MAX][2][CT];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15;
+    const int n = blockIdx.x / d.n_chunk_max;
+    const int c = blockIdx.x - n * d.n_chunk_max;
+    const int j = blockIdx.y;
+    const int cu0 = p.cu[n];
+    const int T_n = p.cu[n + 1] - cu0;
+    if (c * CT >= T_n) return;
+    const int nv = min(CT, T_n - c * CT);
+    const int64_t tb = (int64_t)cu0 + c * CT;
+    const int hk = d.hk, hv = d.hv, G = d.G, C = d.C;
+    const TI *qkv = static_cast<const TI *>(p.qkv);
+    const TI *cw = static_cast<const TI *>(p.conv_w);
+    TI *hist = static_cast<TI *>(p.hist) + (int64_t)n * 3 * C;
+
+    // gates of the group's value heads, token t of head gh at sGate[gh][.][t]
+    for (int i = tid; i < G * CT; i += CHUNK_PREP_THREADS) {
+        const int gh = i / CT, t = i - gh * CT, h = j * G + gh;
+        float g = 0.f, bt = 0.f;
+        if (t < nv) {
+            const int64_t e = (tb + t) * hv + h;
+            gates(ld1(static_cast<const TI *>(p.a) + e), ld1(static_cast<const TI *>(p.dt_bias) + h),
+                  ld1(static_cast<const TI *>(p.A_log) + h), ld1(static_cast<const TI *>(p.b) + e), g, bt);
+        }
+        sGate[gh][0][t] = g;
+        sGate[gh][1][t] = bt;
+    }
+
+    // Rows (token t, unit u) of 128 channels, 8 per lane in a 16-lane row:
+    // u = 0 q of key head j, u = 1 its k, u = 2 + gh v of value head j G + gh.
+    const int units = 2 + G;
+    auto unit_base = [&](int u) {
+        return u == 0 ? j * 128 : u == 1 ? (hk + j) * 128 : (2 * hk + j * G + (u - 2)) * 128;
+    };
+    // row xi of X = [history (3 rows); the sequence's tokens]
+    auto xrow = [&](int64_t xi, int ch, Raw8<TI> &x) {
+        if (xi < 3) x.load(hist + xi * C + ch);
+        else x.load(qkv + (cu0 + xi - 3) * C + ch);
+    };
+    for (int r = wave * 4 + (lane >> 4); r < CT * units; r += 16) {  // uniform per 16-lane row
+        const int t = r % CT, u = r / CT;
+        const int ch = unit_base(u) + l16 * 8;
+        if (t >= nv) {
+            if (u < 2) {
+                float *dst = u == 0 ? &sm.sQ[t][l16 * 8] : &sm.sK[t][l16 * 8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dst[e] = 0.f;
+            }
+            continue;
+        }
+        float w[8][4];
+        {
+            float tw[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                load8(cw + (int64_t)ch * 4 + k * 8, tw);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = tw[e];
+            }
+        }
+        const int64_t x0 = (int64_t)c * CT + t;  // X row of tap 0
+        Raw8<TI> x[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xrow(x0 + m, ch, x[m]);
+        float sv[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], x[0].get(e), x[1].get(e),
+                                    x[2].get(e), x[3].get(e));
+            sv[e] = silu_fast(acc);
+            ss = fmaf(sv[e], sv[e], ss);
+        }
+        if (u < 2) {
+            ss = row_sum16(ss);
+            const float sc = rsqrt_fast(ss + d.eps_l2);
+            float *dst = u == 0 ? &sm.sQ[t][l16 * 8] : &sm.sK[t][l16 * 8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[e] = sv[e] * sc;
+        } else {
+            store8(p.vc + ((tb + t) * hv + j * G + (u - 2)) * 128 + l16 * 8, sv);
+        }
+    }
+    __syncthreads();
+
+    // the new history of this block's channels (chunk 0 only)
+    if (c == 0 && tid < units * 16) {
+        const int ch = unit_base(tid >> 4) + l16 * 8;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            // X row T_n + r; for T_n + r < 3 it is old history row T_n + r > r,
+            // not yet overwritten
+            Raw8<TI> v;
+            xrow((int64_t)T_n + r, ch, v);
+            v.store(hist + (int64_t)r * C + ch);
+        }
+    }
+
+    auto load_gb = [&](int gh, float &gl, float &bl) {
+        gl = sGate[gh][0][l16];
+        bl = sGate[gh][1][l16];
+    };
+    float g_next = 0.f, b_next = 0.f;
+    if (wave < G) load_gb(wave, g_next, b_next);
+    prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c), nv, g_next, b_next, load_gb);
+}
+
+static PrepDims prep_dims(const gdn_shape &s)
+{
     PrepDims pd;
     pd.hk = s.hk;
     pd.hv = s.hv;
     pd.G = s.hv / s.hk;
     pd.n_chunk_max = (int)((s.max_T + CT - 1) / CT);
-    pd.vh_base = vh_base;
+    pd.vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
     pd.m1 = -1.f;
-    hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk),
-                       dim3(256), 0, st, a, pd);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    pd.C = 2 * s.hk * 128 + s.hv * 128;
+    pd.eps_l2 = s.eps_l2;
+    return pd;
+}
+
+static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
+{
     ChunkDims cd;
     cd.hk = s.hk;
     cd.hv = s.hv;
     cd.G = s.hv / s.hk;
-    cd.vh_base = vh_base;
+    cd.vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
     cd.m1 = -1.f;
     const int64_t blocks = (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS);
     hipLaunchKernelGGL(scan_chunk_kernel, dim3((unsigned)blocks), dim3(CHUNK_THREADS), 0, st, a, cd);
     return hipGetLastError();
+}
+
+hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
+{
+    const PrepDims pd = prep_dims(s);
+    hipLaunchKernelGGL(scan_prep_kernel, dim3((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk),
+                       dim3(CHUNK_PREP_THREADS), 0, st, a, pd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_chunk(s, a, st);
+}
+
+hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const ScanArgs &a,
+                             hipStream_t st)
+{
+    const PrepDims pd = prep_dims(s);
+    const dim3 grid((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk);
+    if (s.io_dtype == GDN_F16)
+        hipLaunchKernelGGL(layer_prep_kernel<_Float16>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+    else
+        hipLaunchKernelGGL(layer_prep_kernel<float>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_chunk(s, a, st);
 }
 
 size_t scan_workspace_bytes(const gdn_shape &s)
