@@ -700,21 +700,10 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
     const TI *cw = static_cast<const TI *>(p.conv_w);
     TI *hist = static_cast<TI *>(p.hist) + (int64_t)n * 3 * C;
 
-    // gates of the group's value heads, token t of head gh at sGate[gh][.][t]
-    for (int i = tid; i < G * CT; i += CHUNK_PREP_THREADS) {
-        const int gh = i / CT, t = i - gh * CT, h = j * G + gh;
-        float g = 0.f, bt = 0.f;
-        if (t < nv) {
-            const int64_t e = (tb + t) * hv + h;
-            gates(ld1(static_cast<const TI *>(p.a) + e), ld1(static_cast<const TI *>(p.dt_bias) + h),
-                  ld1(static_cast<const TI *>(p.A_log) + h), ld1(static_cast<const TI *>(p.b) + e), g, bt);
-        }
-        sGate[gh][0][t] = g;
-        sGate[gh][1][t] = bt;
-    }
-
-    // Rows (token t, unit u) of 128 channels, 8 per lane in a 16-lane row:
-    // u = 0 q of key head j, u = 1 its k, u = 2 + gh v of value head j G + gh.
+    // Tasks (unit u, half hf) of 8 tokens x 128 channels, one per 16-lane row,
+    // 8 channels per lane: u = 0 q of key head j, u = 1 its k, u = 2 + gh v of
+    // value head j G + gh.  A task loads its weights once and its 11 rows of
+    // X up front, then walks the 8 tokens.
     const int units = 2 + G;
     auto unit_base = [&](int u) {
         return u == 0 ? j * 128 : u == 1 ? (hk + j) * 128 : (2 * hk + j * G + (u - 2)) * 128;
@@ -724,17 +713,12 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
         if (xi < 3) x.load(hist + xi * C + ch);
         else x.load(qkv + (cu0 + xi - 3) * C + ch);
     };
-    for (int r = wave * 4 + (lane >> 4); r < CT * units; r += 16) {  // uniform per 16-lane row
-        const int t = r % CT, u = r / CT;
+    const int ntask = 2 * units;
+    for (int task = wave * 4 + (lane >> 4); task < ntask; task += 16) {  // uniform per 16-lane row
+        const int u = task >> 1, hf = task & 1;
         const int ch = unit_base(u) + l16 * 8;
-        if (t >= nv) {
-            if (u < 2) {
-                float *dst = u == 0 ? &sm.sQ[t][l16 * 8] : &sm.sK[t][l16 * 8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dst[e] = 0.f;
-            }
-            continue;
-        }
+        const int t0 = 8 * hf;
+        const int nt = max(0, min(8, nv - t0));  // valid tokens of this task
         float w[8][4];
         {
             float tw[8];
@@ -745,27 +729,51 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
                 for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = tw[e];
             }
         }
-        const int64_t x0 = (int64_t)c * CT + t;  // X row of tap 0
-        Raw8<TI> x[4];
+        const int64_t xb = (int64_t)c * CT + t0;  // X row of tap 0 of the first token
+        Raw8<TI> x[11];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) xrow(x0 + m, ch, x[m]);
-        float sv[8];
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], x[0].get(e), x[1].get(e),
-                                    x[2].get(e), x[3].get(e));
-            sv[e] = silu_fast(acc);
-            ss = fmaf(sv[e], sv[e], ss);
+        for (int i = 0; i < 11; ++i) {
+            if (i < nt + 3) xrow(xb + i, ch, x[i]);
+            else x[i].zero();
         }
-        if (u < 2) {
-            ss = row_sum16(ss);
-            const float sc = rsqrt_fast(ss + d.eps_l2);
-            float *dst = u == 0 ? &sm.sQ[t][l16 * 8] : &sm.sK[t][l16 * 8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dst[e] = sv[e] * sc;
-        } else {
-            store8(p.vc + ((tb + t) * hv + j * G + (u - 2)) * 128 + l16 * 8, sv);
+        for (int i = 0; i < 8; ++i) {
+            const int t = t0 + i;
+            float sv[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], x[i].get(e),
+                                        x[i + 1].get(e), x[i + 2].get(e), x[i + 3].get(e));
+                sv[e] = silu_fast(acc);
+                ss = fmaf(sv[e], sv[e], ss);
+            }
+            if (u < 2) {
+                ss = row_sum16(ss);
+                const float sc = rsqrt_fast(ss + d.eps_l2);
+                float *dst = u == 0 ? &sm.sQ[t][l16 * 8] : &sm.sK[t][l16 * 8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dst[e] = i < nt ? sv[e] * sc : 0.f;
+            } else if (i < nt) {
+                store8(p.vc + ((tb + t) * hv + j * G + (u - 2)) * 128 + l16 * 8, sv);
+            }
+        }
+    }
+
+    // gates of the group's value heads, token t of head gh at sGate[gh][.][t]
+    // (the last wave, which has the fewest tasks above)
+    if (wave == CHUNK_PREP_THREADS / 64 - 1) {
+        for (int i = lane; i < G * CT; i += 64) {
+            const int gh = i / CT, t = i - gh * CT, h = j * G + gh;
+            float g = 0.f, bt = 0.f;
+            if (t < nv) {
+                const int64_t e = (tb + t) * hv + h;
+                gates(ld1(static_cast<const TI *>(p.a) + e), ld1(static_cast<const TI *>(p.dt_bias) + h),
+                      ld1(static_cast<const TI *>(p.A_log) + h), ld1(static_cast<const TI *>(p.b) + e), g,
+                      bt);
+            }
+            sGate[gh][0][t] = g;
+            sGate[gh][1][t] = bt;
         }
     }
     __syncthreads();
