@@ -432,9 +432,10 @@ struct ChunkDims {
 // A block owns 32 value channels of one (sequence, value head): two row groups
 // of 16 channels, and each row group is shared by a pair of waves, one per half
 // of the 128 keys; each of these four compute waves holds its 16 x 64 quarter
-// of the block's state.  A fifth wave only copies operands into LDS.
+// of the block's state.  A fifth wave only copies operands into LDS, and a
+// sixth forms the outputs from what the compute waves leave in LDS.
 constexpr int CHUNK_WAVES = 4;                       // compute waves: 2 row groups x 2 key halves
-constexpr int CHUNK_THREADS = 64 * (CHUNK_WAVES + 1); // + the copy wave
+constexpr int CHUNK_THREADS = 64 * (CHUNK_WAVES + 2); // + the copy wave and the output wave
 constexpr int CHUNK_ROWS = 32;                       // value channels per block
 constexpr int NBUF = 4;                              // LDS copies of a chunk's operands
 
@@ -451,15 +452,33 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The copy and output waves' side of the same barrier.  They write LDS only
+// through the copies, whose completion the copy wave waits for explicitly
+// (vmcnt) before arriving; their own LDS reads are waited for here.  The
+// empty asm statements keep the compiler from moving memory operations
+// across the barrier.  (The fenced form above would also wait for global
+// stores and loads in flight, which the compute waves do not need.)
+__device__ __forceinline__ void side_barrier()
+{
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
 {
     // operands of four chunks in flight: key-head slot, value-head slot, v
     __shared__ __attribute__((aligned(16))) float sKH[NBUF][SCAN_KH_FLOATS];
     __shared__ __attribute__((aligned(16))) float sVH[NBUF][SCAN_SLOT_FLOATS];
     __shared__ __attribute__((aligned(16))) float sV[NBUF][CT][CHUNK_ROWS];
-    // partial K S^T of every compute wave, partial Q S^T of the upper-key waves
+    // partial K S^T and Q S^T of every compute wave, and U of each row group
     __shared__ __attribute__((aligned(16))) f4 sXP[2][CHUNK_WAVES][64];
-    __shared__ __attribute__((aligned(16))) f4 sXR[2][CHUNK_WAVES / 2][64];
+    __shared__ __attribute__((aligned(16))) f4 sXR[2][CHUNK_WAVES][64];
+    __shared__ __attribute__((aligned(16))) f4 sU[2][CHUNK_WAVES / 2][64];
+    // Lam and M of the chunk, passed on to the copy wave
+    __shared__ __attribute__((aligned(16))) f4 sLam[2][64];
+    __shared__ __attribute__((aligned(16))) h8 sMp[2][64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -491,7 +510,8 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         typedef void __attribute__((address_space(3))) *lptr_t;
         constexpr int KH_PIECES = SCAN_KH_FLOATS * 4 / 1024;                       // 24
         constexpr int VH_PIECES = (SCAN_SLOT_FLOATS * 4 + 1023) / 1024;             // 3
-        constexpr int VH_TAIL = (SCAN_SLOT_FLOATS * 4 - (VH_PIECES - 1) * 1024) / 16;  // 16 lanes
+        // the last value-head piece is 256 bytes: one dword per lane
+        static_assert(SCAN_SLOT_FLOATS * 4 - (VH_PIECES - 1) * 1024 == 256, "value-head tail");
         constexpr int V_PIECES = CT * CHUNK_ROWS * 4 / 1024;                        // 2
         constexpr int V_LANES = CHUNK_ROWS / 4;                                     // lanes per token
         constexpr int PER_CHUNK = KH_PIECES + VH_PIECES + V_PIECES;                 // copies per chunk
@@ -499,6 +519,9 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         static_assert(2 * PER_CHUNK <= 63, "vmcnt range");
         auto copy16 = [](const float *src, float *lds_piece) {
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_piece, 16, 0, 0);
+        };
+        auto copy4 = [](const float *src, float *lds_piece) {
+            __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_piece, 4, 0, 0);
         };
         // Rows past the sequence's end read its last token (valid memory); the
         // slots give them zero weight (beta = Lam = 0, identity rows of T, zero
@@ -511,10 +534,10 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
             const float *khs = p.ws + (slot * hk + j) * SCAN_KH_FLOATS + lane * 4;
 #pragma unroll
             for (int m = 0; m < KH_PIECES; ++m) copy16(khs + m * 256, &sKH[b][m * 256]);
-            const float *vhs = p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS + lane * 4;
+            const float *vhs = p.ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS;
 #pragma unroll
-            for (int m = 0; m < VH_PIECES - 1; ++m) copy16(vhs + m * 256, &sVH[b][m * 256]);
-            if (lane < VH_TAIL) copy16(vhs + (VH_PIECES - 1) * 256, &sVH[b][(VH_PIECES - 1) * 256]);
+            for (int m = 0; m < VH_PIECES - 1; ++m) copy16(vhs + m * 256 + lane * 4, &sVH[b][m * 256]);
+            copy4(vhs + (VH_PIECES - 1) * 256 + lane, &sVH[b][(VH_PIECES - 1) * 256]);
             const float *vb = p.vc + (tb * hv + h) * 128 + rb * CHUNK_ROWS + (lane % V_LANES) * 4;
 #pragma unroll
             for (int m = 0; m < V_PIECES; ++m) {
@@ -528,9 +551,9 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         for (int c = 0; c < 3 && c < n_chunks; ++c) issue(c);
         if (n_chunks > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_CHUNK));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        lds_barrier();
+        side_barrier();
         for (int c = 0; c < n_chunks; ++c) {
-            lds_barrier();
+            side_barrier();
             if (c + 3 < n_chunks) {
                 issue(c + 3);
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_CHUNK));  // chunk c + 2 has landed
@@ -538,6 +561,47 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
         }
+        side_barrier();
+        return;
+    }
+    if (wave == CHUNK_WAVES + 1) {
+        // ---- output wave: O = (Lam R + M U) / sqrt(dk) of chunk c for both
+        // row groups, after the barrier of step c + 1.  R, U, Lam and M come
+        // from the compute waves through LDS: written after the barrier of
+        // step c, overwritten (for chunk c + 2) only after that of step c + 2.
+        // None of them is an LDS target of the copies.  A wave of its own, as
+        // the copy wave spends most of a step issuing the copies.
+        auto o_store = [&](int c) {
+            const int x = c & 1;
+            const int nv = min(CT, T_n - c * CT);
+            const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
+            const f4 lam = sLam[x][lane];
+            const h8 mp = sMp[x][lane];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const f4 R = sXR[x][2 * g][lane] + sXR[x][2 * g + 1][lane];
+                const f4 U = sU[x][g][lane];
+                h4 uh, ul;
+                split4(U, uh, ul, d.m1);
+                f4 O = lam * R;
+                O = mfma_k32(mp, cat(uh, uh), O);
+                O = mfma_k16(lo_half(mp), ul, O);
+                O *= SCALE;
+                char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + g * 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 4 * kk + r;
+                    if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r];
+                }
+            }
+        };
+        side_barrier();
+        for (int c = 0; c < n_chunks; ++c) {
+            side_barrier();
+            if (c > 0) o_store(c - 1);
+        }
+        side_barrier();
+        o_store(n_chunks - 1);
         return;
     }
 
@@ -555,27 +619,33 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
 #pragma unroll
     for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b) * KQ_SCALE;
 
-    auto step = [&](int c) {
-        const int b = c & (NBUF - 1), x = c & 1;
-        const int nv = min(CT, T_n - c * CT);
-        const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
-        const _Float16 *khp = reinterpret_cast<const _Float16 *>(sKH[b]);
-        const float *vh = sVH[b];
-        // operands of this chunk: K and Q for this wave's two 32-key steps
-        h8 kph[2], kpl[2], qph[2], qpl[2];
+    // this wave's two 32-key steps of K (or Q) of chunk c, hi and lo
+    auto key_ops = [&](int c, int off, h8 (&hi)[2], h8 (&lo)[2]) {
+        const _Float16 *khp = reinterpret_cast<const _Float16 *>(sKH[c & (NBUF - 1)]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int s = 2 * kh + i;
-            kph[i] = *reinterpret_cast<const h8 *>(khp + KH_KP + ((s * 2 + 0) * 64 + lane) * 8);
-            kpl[i] = *reinterpret_cast<const h8 *>(khp + KH_KP + ((s * 2 + 1) * 64 + lane) * 8);
-            qph[i] = *reinterpret_cast<const h8 *>(khp + KH_QP + ((s * 2 + 0) * 64 + lane) * 8);
-            qpl[i] = *reinterpret_cast<const h8 *>(khp + KH_QP + ((s * 2 + 1) * 64 + lane) * 8);
+            hi[i] = *reinterpret_cast<const h8 *>(khp + off + ((s * 2 + 0) * 64 + lane) * 8);
+            lo[i] = *reinterpret_cast<const h8 *>(khp + off + ((s * 2 + 1) * 64 + lane) * 8);
         }
-        // partial P = K S^T and R = Q S^T (x256) over this wave's 64 keys
+    };
+
+    // K of chunk c + 1 is read from LDS during step c (it landed before the
+    // barrier of step c), and the partial R of chunk c is formed after the
+    // state update of step c: neither is on the path from the barrier of one
+    // step to that of the next.
+    lds_barrier();  // chunks 0 and 1 are in LDS
+    h8 kph[2], kpl[2];
+    key_ops(0, KH_KP, kph, kpl);
+    for (int c = 0; c < n_chunks; ++c) {
+        const int b = c & (NBUF - 1), x = c & 1;
+        const _Float16 *khp = reinterpret_cast<const _Float16 *>(sKH[b]);
+        const float *vh = sVH[b];
+        // partial P = K S^T (x256) over this wave's 64 keys
         h8 sh[2], sl[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) split8(S4[2 * i], S4[2 * i + 1], sh[i], sl[i], d.m1);
-        f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh, Rhh = Phh, Rhl = Phh, Rlh = Phh;
+        f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             Phh = mfma_k32(kph[i], sh[i], Phh);
@@ -584,19 +654,12 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         }
         const f4 Pp = (Phh + Phl) + Plh;
         sXP[x][wave][lane] = Pp;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            Rhh = mfma_k32(qph[i], sh[i], Rhh);
-            Rhl = mfma_k32(qph[i], sl[i], Rhl);
-            Rlh = mfma_k32(qpl[i], sh[i], Rlh);
-        }
-        const f4 Rp = (Rhh + Rhl) + Rlh;
-        if (kh == 1) sXR[x][grp][lane] = Rp;
         lds_barrier();  // partials visible; every wave is past chunk c - 1
+        __builtin_amdgcn_sched_barrier(0);  // nothing below moves up before the barrier
 
-        // the full P, summed in the same order by both waves of the pair
+        // the partner's partial P first, then this chunk's value-head
+        // operands, its Q and K^T, and K of the next chunk
         const f4 Po = sXP[x][partner][lane];
-        const f4 P = kh == 0 ? Pp + Po : Po + Pp;
         const h8 tp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_TP) + lane * 8);
         const f4 lam = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
         const f4 bet = *reinterpret_cast<const f4 *>(vh + VH_BETA + 4 * kk);
@@ -605,6 +668,16 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         f4 vv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) vv[r] = sV[b][4 * kk + r][grp * 16 + l16];
+        h8 kt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kt[i] = *reinterpret_cast<const h8 *>(khp + KH_KT + ((4 * kh + i) * 64 + lane) * 8);
+        h8 qph[2], qpl[2];
+        key_ops(c, KH_QP, qph, qpl);
+        if (c + 1 < n_chunks) key_ops(c + 1, KH_KP, kph, kpl);
+        __builtin_amdgcn_sched_barrier(0);  // the reads go out before the work below
+
+        // the full P, summed in the same order by both waves of the pair
+        const f4 P = kh == 0 ? Pp + Po : Po + Pp;
         // B = beta (V - Lam P), component r is token 4 kk + r, channel l16
         f4 Bm;
 #pragma unroll
@@ -614,50 +687,34 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo
         const f4 z4 = {0.f, 0.f, 0.f, 0.f};
         const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4);
+        if (kh == 0) sU[x][grp][lane] = U;
+        if (wave == 1) {
+            sLam[x][lane] = lam;
+            sMp[x][lane] = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
+        }
         h4 uwh, uwl;
         split4(U * wu, uwh, uwl, d.m1);
         const h8 uww = cat(uwh, uwh);
-        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks,
-        // with the output of the lower-key wave of the pair,
-        // O = (Lam R + M U) / sqrt(dk), issued between them (off the chain to
-        // the next chunk)
-        auto update = [&](int i) {
-            const h8 kt = *reinterpret_cast<const h8 *>(khp + KH_KT + ((4 * kh + i) * 64 + lane) * 8);
+        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             f4 C = S4[i] * last;
-            C = mfma_k32(kt, uww, C);
-            C = mfma_k16(lo_half(kt), uwl, C);
+            C = mfma_k32(kt[i], uww, C);
+            C = mfma_k16(lo_half(kt[i]), uwl, C);
             S4[i] = C;
-        };
-        update(0);
-        update(1);
-        if (kh == 0) {
-            const f4 R = Rp + sXR[x][grp][lane];
-            const h8 mp = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
-            h4 uh, ul;
-            split4(U, uh, ul, d.m1);
-            f4 O = lam * R;
-            O = mfma_k32(mp, cat(uh, uh), O);
-            O = mfma_k16(lo_half(mp), ul, O);
-            O *= SCALE;
-            char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + grp * 16);
-            if (nv == CT) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    *reinterpret_cast<float *>(ob + ((uint32_t)(4 * kk + r) * vstride + l16) * 4u) = O[r];
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * kk + r;
-                    if (t < nv) *reinterpret_cast<float *>(ob + ((uint32_t)t * vstride + l16) * 4u) = O[r];
-                }
-            }
         }
-        update(2);
-        update(3);
-    };
-
-    lds_barrier();  // chunks 0 and 1 are in LDS
-    for (int c = 0; c < n_chunks; ++c) step(c);
+        // partial R = Q S^T (x256) of this chunk from the split of the state
+        // before the update; the output wave reads it after the next barrier
+        f4 Rhh = z4, Rhl = z4, Rlh = z4;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            Rhh = mfma_k32(qph[i], sh[i], Rhh);
+            Rhl = mfma_k32(qph[i], sl[i], Rhl);
+            Rlh = mfma_k32(qpl[i], sh[i], Rlh);
+        }
+        sXR[x][wave][lane] = (Rhh + Rhl) + Rlh;
+    }
+    lds_barrier();  // R and U of the last chunk are visible to the output wave
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<f4 *>(Srow + 16 * i) = S4[i] * (1.f / KQ_SCALE);
 }
