@@ -41,23 +41,27 @@
 //   - per value head: the decays, T = (I + A)^-1 by forward substitution
 //     (one column per lane, in registers), M, Lam, beta and the last-row
 //     decays, T and M split and laid out as MFMA operands ("value-head slot").
-// * gdn_scan_chunk (sequential over chunks): a block of 4 waves owns 64 value
-//   channels of one (sequence, value head), one wave per SIMD (two waves per
-//   SIMD measured slower: the SIMD's MFMA and VALU issue are the limit, not
-//   latency alone); each wave holds 16 channels x all 128 keys of the state in
-//   MFMA accumulator layout (32 VGPRs/lane), so no partial sums cross waves.
-//   Per chunk and wave:
-//     K S^T, Q S^T    12 + 12  v_mfma_f32_16x16x32_f16 (3 split terms x 4 key steps)
+// * gdn_scan_chunk (sequential over chunks): a block owns 32 value channels
+//   of one (sequence, value head) in two row groups of 16; each row group's
+//   state (16 channels x 128 keys) is split by key halves over a pair of
+//   compute waves, each holding its 16 x 64 quarter in MFMA accumulator
+//   layout (16 VGPRs/lane).  Per chunk and compute wave:
+//     K S^T, Q S^T     6 + 6    v_mfma_f32_16x16x32_f16 (3 split terms x 2 key steps)
 //     U = T B          1 + 1    16x16x32 (hi.hi + lo.hi) + 16x16x16 (hi.lo)
-//     O = Lam R + M U  1 + 1    same
-//     S' = Lam_last S + K^T (D U)  8 + 8  same, per key block
+//     S' = Lam_last S + K^T (D U)  4 + 4  same, per key block
 //   (over the 16 tokens of a chunk, two split terms share one 16x16x32 product:
-//   its contraction runs over the pair (term, token))
+//   its contraction runs over the pair (term, token)).  The two waves of a
+//   pair add their partial K S^T through LDS in the same order, so both form
+//   the same U; this exchange and one barrier per chunk are the only
+//   synchronisation on the recurrence.
 //   Every product consumes the accumulator layout the previous one produced
 //   (the contraction index is permuted consistently, and the prep kernel packs
 //   K, Q and K^T in that order), so the state never leaves registers.
 //   A copy wave moves the chunk operands from global memory into LDS three
-//   chunks ahead (four LDS copies); one barrier per chunk.
+//   chunks ahead (four LDS copies).  An output wave forms O = Lam R + M U
+//   (1 + 1 products per row group) one step behind, from the partial Q S^T,
+//   U, Lam and M the compute waves leave in LDS, so the outputs stay off the
+//   recurrence's path.
 // * Block order is XCD-aware: blocks are dealt round-robin to the 8 XCDs, so
 //   the index is permuted to give each XCD whole key-head groups, whose
 //   key-head slots are then shared in one L2.
