@@ -105,6 +105,11 @@ __device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c)
 }
 // D += A B, 16x16x16: lane l supplies A[l%16][4(l/16)+e] and B[4(l/16)+e][l%16];
 // D[4(l/16)+r][l%16] comes back in component r.
+// A product never takes the result of a product of the other shape as its
+// accumulator: the compiler leaves too few wait states between a 16x16x32
+// and a 16x16x16 that reads its result as C on gfx950 (measured: stale rows
+// in the result).  Chains stay within one shape; the two shapes meet only
+// through a VALU add, or the 16-deep term runs as a zero-padded 16x16x32.
 __device__ __forceinline__ f4 mfma_k16(h4 a, h4 b, f4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -487,6 +492,7 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
 
     // XCD-aware work index -> (sequence n, value head h, channel block rb)
     constexpr int RB = 128 / CHUNK_ROWS;
@@ -587,9 +593,9 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
                 const f4 U = sU[x][g][lane];
                 h4 uh, ul;
                 split4(U, uh, ul, d.m1);
-                f4 O = lam * R;
-                O = mfma_k32(mp, cat(uh, uh), O);
-                O = mfma_k16(lo_half(mp), ul, O);
+                const h4 zh = {};
+                f4 O = mfma_k32(mp, cat(uh, uh), lam * R);
+                O = mfma_k32(cat(lo_half(mp), zh), cat(ul, zh), O);
                 O *= SCALE;
                 char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + g * 16);
 #pragma unroll
@@ -689,7 +695,6 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         h4 bh, bl;
         split4(Bm, bh, bl, d.m1);
         // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo
-        const f4 z4 = {0.f, 0.f, 0.f, 0.f};
         const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4);
         if (kh == 0) sU[x][grp][lane] = U;
         if (wave == 1) {
@@ -699,13 +704,14 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         h4 uwh, uwl;
         split4(U * wu, uwh, uwl, d.m1);
         const h8 uww = cat(uwh, uwh);
-        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks
+        // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks;
+        // the hi.lo term runs as a zero-padded 16x16x32 chained on the first
+        // product (see mfma_k16)
+        const h4 zh = {};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f4 C = S4[i] * last;
-            C = mfma_k32(kt[i], uww, C);
-            C = mfma_k16(lo_half(kt[i]), uwl, C);
-            S4[i] = C;
+            const f4 C = mfma_k32(kt[i], uww, S4[i] * last);
+            S4[i] = mfma_k32(cat(lo_half(kt[i]), zh), cat(uwl, zh), C);
         }
         // partial R = Q S^T (x256) of this chunk from the split of the state
         // before the update; the output wave reads it after the next barrier
