@@ -272,25 +272,39 @@ def main():
         y = torch.empty((batch, hv * 128), dtype=torch.float16, device=dev)
 
         def one():
+            # on the current stream: the capture stream while a graph is captured
             for d in ls:
                 B.gdn_step(shape, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"],
-                           d["z"], d["gamma"], d["hist"], d["S0"], y, stream=stream)
+                           d["z"], d["gamma"], d["hist"], d["S0"], y)
+        def timed(fn):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (steps * layers)
+
         for _ in range(3):
             one()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
+        us = timed(one)
+        # the same 36-layer step captured once in a HIP graph (no host
+        # launches per layer), replayed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
             one()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (steps * layers)
+        graph.replay()
+        us_g = timed(graph.replay)
         C = 2 * hk * 128 + hv * 128
         byts = batch * (2 * hv * 128 * 128 * 4 + C * 2 + 4 * 3 * C * 2 + 2 * hv * 2 + 2 * hv * 128 * 2)
         return {"batch": batch, "us_per_layer": round(us, 2),
                 "tokens_per_s": round(batch / (us * 1e-6 * layers), 1),
-                "bytes_per_layer": byts, "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                "us_per_layer_graph": round(us_g, 2),
+                "tokens_per_s_graph": round(batch / (us_g * 1e-6 * layers), 1),
+                "bytes_per_layer": byts, "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "hbm_frac_graph": round(byts / (us_g * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     log("timing gdn_step decode")
     dec = [decode(b) for b in (1, 8, 64)]

@@ -104,3 +104,45 @@ def test_step_is_bitwise_deterministic(gpu):
         torch.cuda.synchronize()
         outs.append((np_(buf.y).view(np.uint16), np_(buf.state).view(np.uint32)))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_step_graph_replay_matches_eager(gpu):
+    # A decode step over 4 layers (each with its own weights, state and
+    # history) captured once in a HIP graph and replayed three times from the
+    # same initial state and history, with eager copies and a synchronisation
+    # between the replays: every replay equals the eager run bit for bit.
+    L = 4
+    w = synth.Workload("step_graph", hk=16, hv=48, seqlens=(1,) * 8, seed=(34,), s0_std=0.05,
+                       hist_std=1.0)
+    bufs = [LayerBuffers.create(w, synth.layer_inputs(w, l)) for l in range(L)]
+    init = [(b.state.clone(), b.hist.clone()) for b in bufs]
+
+    def run_all():
+        for b in bufs:
+            _step(b)
+
+    def restore():
+        for b, (s, h) in zip(bufs, init):
+            b.state.copy_(s)
+            b.hist.copy_(h)
+
+    banner("gdn_step", w.name, "eager")
+    run_all()
+    torch.cuda.synchronize()
+    ref = [(np_(b.y).copy(), np_(b.state).copy(), np_(b.hist).copy()) for b in bufs]
+    restore()
+    torch.cuda.synchronize()
+    banner("gdn_step", w.name, "capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        banner("gdn_step", w.name, f"replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for b, (y, s, h) in zip(bufs, ref):
+            assert np.array_equal(np_(b.y).view(np.uint16), y.view(np.uint16)), f"y, replay {rep}"
+            assert np.array_equal(np_(b.state).view(np.uint32), s.view(np.uint32)), f"state, replay {rep}"
+            assert np.array_equal(np_(b.hist).view(np.uint16), h.view(np.uint16)), f"hist, replay {rep}"
