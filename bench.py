@@ -190,40 +190,53 @@ def main():
         return dict(ms_per_step=e0.elapsed_time(e1) / steps)
 
     def run(out, steps, warmup):
-        # the staged path (gdn_pre, gdn_scan, gdn_post per layer) with HIP events
-        # between the stages, for the per-stage times and the scan's roofline
+        # the staged path (gdn_pre, gdn_scan, gdn_post per layer): the whole pass
+        # timed as one, then each stage alone over the 36 layers back to back
+        # (one event pair per stage loop: the per-launch average of that
+        # kernel, without events between launches), for the per-stage times
+        # and the scan's roofline
         ys = [torch.empty((T, hv * 128), dtype=TORCH_DTYPE[out], device=dev) for _ in range(L)]
         shape = B.make_shape(hk, hv, 1, T, T, io="f16", out=out)
         sws = scratch(B.gdn_scan_workspace_bytes(shape), dev)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L * steps)]
 
-        def step(events=None):
+        def pre(d):
+            B.gdn_pre(shape, cu, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                      d["hist"], qn, kn, vc, g, beta, stream=stream)
+
+        def scan(d):
+            B.gdn_scan(shape, cu, qn, kn, vc, g, beta, d["S0"], o, sws, stream=stream)
+
+        def post(d, l):
+            B.gdn_post(shape, o, d["z"], d["gamma"], ys[l], stream=stream)
+
+        def step():
             for l, d in enumerate(layers):
-                e = events[l] if events else None
-                if e: e[0].record(stream)
-                B.gdn_pre(shape, cu, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"],
-                          d["dt_bias"], d["hist"], qn, kn, vc, g, beta, stream=stream)
-                if e: e[1].record(stream)
-                B.gdn_scan(shape, cu, qn, kn, vc, g, beta, d["S0"], o, sws, stream=stream)
-                if e: e[2].record(stream)
-                B.gdn_post(shape, o, d["z"], d["gamma"], ys[l], stream=stream)
-                if e: e[3].record(stream)
+                pre(d)
+                scan(d)
+                post(d, l)
+
+        def timed(fn, n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
 
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_start.record(stream)
-        for s in range(steps):
-            step(ev[s * L:(s + 1) * L])
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t_start.elapsed_time(t_end)
-        pre = np.mean([e[0].elapsed_time(e[1]) for e in ev])
-        scan = np.mean([e[1].elapsed_time(e[2]) for e in ev])
-        post = np.mean([e[2].elapsed_time(e[3]) for e in ev])
-        return dict(ms_per_step=total_ms / steps, pre_ms=pre, scan_ms=scan, post_ms=post)
+        total_ms = timed(step, steps)
+        per = {}
+        for name, fn in (("pre", lambda: [pre(d) for d in layers]),
+                         ("scan", lambda: [scan(d) for d in layers]),
+                         ("post", lambda: [post(d, l) for l, d in enumerate(layers)])):
+            fn()
+            torch.cuda.synchronize()
+            per[name] = timed(fn, steps) / L
+        return dict(ms_per_step=total_ms, pre_ms=per["pre"], scan_ms=per["scan"], post_ms=per["post"])
 
     log("timing the layer path, fp16 output")
     l16 = run_layer("f16", args.steps, args.warmup)

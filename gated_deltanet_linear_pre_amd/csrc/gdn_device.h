@@ -29,6 +29,18 @@ __device__ __forceinline__ float row_sum16(float x)
     return x;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt
+// left at their maximum, i.e. not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait for every vector-memory operation this wave has issued.  A kernel that
+// issues all its loads first and then calls this before its first store keeps
+// the compiler from waiting on earlier stores later on: with loads and stores
+// outstanding together, the compiler cannot count either in order and waits
+// for everything (vmcnt(0)) wherever a loaded value is next used.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
+
 // ---- fast elementwise functions on the hardware transcendental unit -------
 // e^x = 2^(x log2 e) on v_exp_f32 (about 1 ulp of the power of two, plus the
 // rounding of x log2 e: relative error below 1e-6 for |x| < 40).
@@ -47,11 +59,14 @@ __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_r
 
 // ---- per-element arithmetic of the pre stage, shared by every kernel that
 // runs it (one expression, so the compiler rounds it the same way everywhere)
-// 4-tap conv of one channel: taps in order, tap 3 on the current token
+// 4-tap conv of one channel: taps in order, tap 3 on the current token.  The
+// first tap is w0 x0 + 0 (equal to w0 x0, but a product of -0 becomes +0): as
+// a fused multiply-add it, like the other three, takes an fp16 x straight
+// from its packed register (v_fma_mix_f32), with no separate conversion.
 __device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, float x0, float x1,
                                        float x2, float x3)
 {
-    float acc = w0 * x0;
+    float acc = fmaf(w0, x0, 0.0f);
     acc = fmaf(w1, x1, acc);
     acc = fmaf(w2, x2, acc);
     acc = fmaf(w3, x3, acc);
@@ -91,6 +106,25 @@ __device__ __forceinline__ void store8(float *__restrict__ p, const float (&x)[8
     reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
+// x[0..3] to p[0..3] and x[4..7] to p[64..67]: the split channel mapping,
+// where the 16 lanes of a row cover channels 0..63 with one instruction and
+// 64..127 with the next
+__device__ __forceinline__ void store8_split(float *__restrict__ p, const float (&x)[8])
+{
+    reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4 *>(p + 64)[0] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// store8_split with non-temporal stores, for outputs no later access of the
+// same kernel reads (they are not kept in the caches on their way out)
+__device__ __forceinline__ void store8_split_nt(float *__restrict__ p, const float (&x)[8])
+{
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const v4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<v4 *>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<v4 *>(p + 64));
+}
+
 // fp32 -> fp16 conversion rounds to nearest even (the default mode).
 __device__ __forceinline__ void store8(_Float16 *__restrict__ p, const float (&x)[8])
 {
@@ -105,18 +139,43 @@ __device__ __forceinline__ float ld1(const _Float16 *p) { return (float)*p; }
 
 // Raw (not widened) storage of 8 elements, kept packed in registers.
 template <typename T> struct Raw8;
+// load_split / store_split: elements 0..3 at p[0..3], 4..7 at p[64..67].
 template <> struct Raw8<_Float16> {
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
     half8 v;
     __device__ __forceinline__ void load(const _Float16 *__restrict__ p) { v = *reinterpret_cast<const half8 *>(p); }
     __device__ __forceinline__ void store(_Float16 *__restrict__ p) const { *reinterpret_cast<half8 *>(p) = v; }
+    __device__ __forceinline__ void load_split(const _Float16 *__restrict__ p)
+    {
+        const half4 a = *reinterpret_cast<const half4 *>(p);
+        const half4 b = *reinterpret_cast<const half4 *>(p + 64);
+        v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    __device__ __forceinline__ void store_split(_Float16 *__restrict__ p) const
+    {
+        *reinterpret_cast<half4 *>(p) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        *reinterpret_cast<half4 *>(p + 64) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+    }
     __device__ __forceinline__ void zero() { v = half8(0); }
     __device__ __forceinline__ float get(int i) const { return (float)v[i]; }
 };
 template <> struct Raw8<float> {
     typedef float f8 __attribute__((ext_vector_type(8), aligned(16)));
+    typedef float f4v __attribute__((ext_vector_type(4)));
     f8 v;
     __device__ __forceinline__ void load(const float *__restrict__ p) { v = *reinterpret_cast<const f8 *>(p); }
     __device__ __forceinline__ void store(float *__restrict__ p) const { *reinterpret_cast<f8 *>(p) = v; }
+    __device__ __forceinline__ void load_split(const float *__restrict__ p)
+    {
+        const f4v a = *reinterpret_cast<const f4v *>(p);
+        const f4v b = *reinterpret_cast<const f4v *>(p + 64);
+        v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    __device__ __forceinline__ void store_split(float *__restrict__ p) const
+    {
+        *reinterpret_cast<f4v *>(p) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        *reinterpret_cast<f4v *>(p + 64) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+    }
     __device__ __forceinline__ void zero() { v = f8(0.f); }
     __device__ __forceinline__ float get(int i) const { return v[i]; }
 };

@@ -30,6 +30,15 @@ constexpr int SCAN_KH_FLOATS = 6144;
 constexpr int SCAN_SLOT_FLOATS = 576;
 size_t scan_workspace_bytes(const gdn_shape &s);
 
+// The layer path with fp16 inputs forms v inside the chunk kernel, from the
+// raw qkv rows of its value channels (4-tap conv with the history, SiLU), and
+// carries the history of those channels there.
+struct VRawArgs {
+    const void *qkv, *conv_w;
+    void *hist;
+    int C;  // channels of a qkv row
+};
+
 // The layer path's fused pre + prep step: the pre-stage inputs, the history
 // (in/out), and the two buffers the chunk kernel reads (vc and the slots).
 struct LayerPrepArgs {
@@ -62,7 +71,6 @@ hipError_t launch_post(const gdn_shape &s, const PostArgs &a, hipStream_t st);
 hipError_t launch_step(const gdn_shape &s, const StepArgs &a, hipStream_t st);
 
 // Grid-size limits the ABI checks before launching.
-constexpr int PRE_TILE_F16 = 16;  // tokens per pre tile, fp16 storage
-constexpr int PRE_TILE_F32 = 8;   // tokens per pre tile, fp32 storage
+constexpr int PRE_WAVE_TOKENS = 4;  // tokens per pre wave; a pre block takes 4 waves' tokens
 
 } // namespace gdn

@@ -14,19 +14,27 @@
 //   hist <- X[T .. T+2]
 //
 // gfx950 mapping.  The stage reads about 21 KB and writes about 41 KB per
-// token at production width, so it is bound by HBM bandwidth.  Channels come in
-// units of one head (128 channels).  A 16-lane DPP row owns one unit, 8
-// consecutive channels per lane, so a wave covers 4 units = 512 channels and
-// each token row arrives as one contiguous 1 KB (fp16) load instruction.  A
-// wave walks a tile of TT tokens.  It loads the TT + 3 rows it needs up front
-// (history rows for the first three tokens of a sequence), slides the 4-tap
-// window in registers, and reduces the q/k sums of squares with a 4-step DPP
-// rotate-add, with no LDS and no barrier.  One extra wave per tile computes the
-// gates of its tokens.
+// token at production width, so it is bound by HBM bandwidth; what sets its
+// speed is how whole its memory instructions are.  Channels come in units of
+// one head (128 channels).  A 16-lane DPP row owns one unit: lane l takes
+// channels 4l..4l+3 and 64+4l..64+4l+3, so each load or store instruction of
+// a wave covers whole 64-channel runs of its 4 units (whole cache lines; with
+// 8 consecutive channels per lane the fp32 stores each wrote half of every
+// line they touched, and ran 15% slower).  A block of 4 waves takes a tile of
+// 4 x 4 tokens of one group of 4 units; each wave loads the 4 + 3 rows its 4
+// tokens need (history rows for the first three tokens of a sequence; the
+// 3-row overlap between waves is an L1/L2 hit), slides the 4-tap window in
+// registers, and reduces the q/k sums of squares with a 4-step DPP rotate-add,
+// with no LDS and no barrier.  One extra row of blocks computes the gates.
+// Every wave issues all its loads before its first store and waits for them
+// once: with loads and stores outstanding together each later use of a loaded
+// value would wait for the stores too.  The outputs go out as non-temporal
+// stores.
 //
-// History carry without a race: only the tile holding tokens 0..TT-1 of a
-// sequence reads the old history (TT >= 3), and that same tile writes the new
-// history, for the same channels and lanes, after its reads.
+// History carry without a race: only the first wave of a sequence reads the
+// old history (its rows 0..2 are X rows 0..2, and every later wave starts at
+// X row 4 or beyond), and that same wave writes the new history, for the same
+// channels and lanes, after its reads.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -34,108 +42,143 @@ namespace gdn {
 
 struct PreDims {
     int hk, hv, C, U;          // U = C / 128 head units
-    int n_ug;                  // unit groups of 4 (waves doing conv)
+    int n_ug;                  // unit groups of 4 (blockIdx.y of the conv blocks)
     int tiles_per_seq;
     float eps;
 };
 
-template <typename TI, int TT>
+// One block per (tile of 4 TW tokens, unit group of 4 units); wave w takes the
+// tile's tokens w TW .. w TW + TW - 1.  blockIdx.y == n_ug: the tile's gates.
+template <typename TI, int TW>
 __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
 {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int wg = blockIdx.y * 4 + wave;  // unit group, or the gates wave
-    if (wg > d.n_ug) return;
-    const int n = blockIdx.x / d.tiles_per_seq;
-    const int tile = blockIdx.x - n * d.tiles_per_seq;
+    static_assert(TW >= 3, "only the first wave of a sequence may read the history");
+    constexpr int TT = 4 * TW;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    // consecutive tiles of one unit group on one XCD (blocks go round-robin
+    // over the 8 XCDs), so a tile's 3-row halo is mostly an L2 hit
+    int bx = blockIdx.x;
+    if ((gridDim.x & 7) == 0) bx = (bx & 7) * (gridDim.x >> 3) + (bx >> 3);
+    const int n = bx / d.tiles_per_seq;
+    const int tile = bx - n * d.tiles_per_seq;
     const int64_t s0 = p.cu[n];
     const int64_t T_n = (int64_t)p.cu[n + 1] - s0;
     const int64_t tau0 = (int64_t)tile * TT;
     if (tau0 >= T_n) return;
-    const int nt = (int)((T_n - tau0) < TT ? (T_n - tau0) : TT);
 
-    if (wg == d.n_ug) {
-        // ---- gates for tokens tau0 .. tau0 + nt - 1 --------------------
+    if ((int)blockIdx.y == d.n_ug) {
+        // ---- gates of the tile's tokens, GB per thread per round; every
+        // load of a round is issued before the round's first store
+        constexpr int GB = 4;
         const TI *a = static_cast<const TI *>(p.a);
         const TI *b = static_cast<const TI *>(p.b);
         const TI *A_log = static_cast<const TI *>(p.A_log);
         const TI *dt_bias = static_cast<const TI *>(p.dt_bias);
         const int hv = d.hv;
-        for (int idx = lane; idx < nt * hv; idx += 64) {
-            const int i = idx / hv;
-            const int h = idx - i * hv;
-            const int64_t e = (s0 + tau0 + i) * hv + h;
-            gates(ld1(a + e), ld1(dt_bias + h), ld1(A_log + h), ld1(b + e), p.g[e], p.beta[e]);
+        const int total = (int)((T_n - tau0) < TT ? (T_n - tau0) : TT) * hv;
+        for (int r0 = 0; r0 < total; r0 += 256 * GB) {  // uniform
+            float av[GB], bv[GB], dv[GB], lv[GB];
+            int64_t e[GB];
+#pragma unroll
+            for (int k = 0; k < GB; ++k) {
+                const int idx = min(r0 + 256 * k + tid, total - 1);
+                const int i = idx / hv, h = idx - i * hv;
+                e[k] = (s0 + tau0 + i) * hv + h;
+                av[k] = ld1(a + e[k]);
+                bv[k] = ld1(b + e[k]);
+                dv[k] = ld1(dt_bias + h);
+                lv[k] = ld1(A_log + h);
+            }
+            wait_vmem_all();
+#pragma unroll
+            for (int k = 0; k < GB; ++k) {
+                float g, bt;
+                gates(av[k], dv[k], lv[k], bv[k], g, bt);
+                if (r0 + 256 * k + tid < total) {
+                    p.g[e[k]] = g;
+                    p.beta[e[k]] = bt;
+                }
+            }
         }
         return;
     }
 
     // ---- conv + SiLU + norm for one unit per 16-lane row ---------------
+    const int64_t t0 = tau0 + wave * TW;  // this wave's first token
+    if (t0 >= T_n) return;                // uniform across the wave
+    const int nt = (int)((T_n - t0) < TW ? (T_n - t0) : TW);
     const TI *qkv = static_cast<const TI *>(p.qkv);
     const TI *cw = static_cast<const TI *>(p.conv_w);
     TI *hist = static_cast<TI *>(p.hist);
     const int C = d.C;
-    const int u = wg * 4 + (lane >> 4);
+    const int u = (int)blockIdx.y * 4 + (lane >> 4);
     const int l16 = lane & 15;
     const bool active = u < d.U;
-    const int c0 = (active ? u : 0) * 128 + l16 * 8;
+    // lane l16 of the row owns channels 4 l16 .. + 3 (values 0..3) and
+    // 64 + 4 l16 .. + 3 (values 4..7) of its unit, so that every load and
+    // store instruction covers whole 64-channel runs of each of its 4 units
+    const int c0 = (active ? u : 0) * 128 + l16 * 4;  // valid for every lane
 
-    // 4 taps of 8 channels = 32 consecutive weights
+    // Every load is unconditional (rows past the last token repeat its row;
+    // inactive rows read unit 0) and all are issued before the first store.
+    // 4 taps of 4 channels = 16 consecutive weights, twice
     float w[8][4];
     {
-        float t[8];
+        float t[4][8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (active) load8(cw + (int64_t)c0 * 4 + k * 8, t);
-            else {
+        for (int k = 0; k < 4; ++k) load8(cw + (int64_t)(c0 + 64 * (k >> 1)) * 4 + (k & 1) * 8, t[k]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) t[e] = 0.f;
-            }
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = t[e];
-        }
+            for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = t[k][e];
     }
-
-    // window rows X[tau0 + r], r = 0 .. TT+2
-    Raw8<TI> win[TT + 3];
+    // window rows X[t0 + r], r = 0 .. TW + 2 (history rows for X index < 3)
+    Raw8<TI> win[TW + 3];
 #pragma unroll
-    for (int r = 0; r < TT + 3; ++r) {
-        const int64_t xi = tau0 + r;
-        if (!active || r >= nt + 3) win[r].zero();
-        else if (xi < 3) win[r].load(hist + ((int64_t)n * 3 + xi) * C + c0);
-        else win[r].load(qkv + (s0 + xi - 3) * C + c0);
+    for (int r = 0; r < TW + 3; ++r) {
+        const int64_t xi = t0 + (r < nt + 3 ? r : nt + 2);
+        const TI *src = xi < 3 ? hist + ((int64_t)n * 3 + xi) * C + c0 : qkv + (s0 + xi - 3) * C + c0;
+        win[r].load_split(src);
     }
+    wait_vmem_all();
 
     // destination of this row's unit
     float *dst;
     int64_t stride;
     const bool is_v = u >= 2 * d.hk;
-    if (u < d.hk) { dst = p.qn + u * 128 + l16 * 8; stride = (int64_t)d.hk * 128; }
-    else if (!is_v) { dst = p.kn + (u - d.hk) * 128 + l16 * 8; stride = (int64_t)d.hk * 128; }
-    else { dst = p.vc + (u - 2 * d.hk) * 128 + l16 * 8; stride = (int64_t)d.hv * 128; }
+    if (u < d.hk) { dst = p.qn + u * 128 + l16 * 4; stride = (int64_t)d.hk * 128; }
+    else if (!is_v) { dst = p.kn + (u - d.hk) * 128 + l16 * 4; stride = (int64_t)d.hk * 128; }
+    else { dst = p.vc + (u - 2 * d.hk) * 128 + l16 * 4; stride = (int64_t)d.hv * 128; }
 
+    auto token = [&](int i) {
+        float s[8];
+        float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < TT; ++i) {
-        if (i < nt) {  // uniform across the wave
-            float s[8];
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], win[i].get(e),
-                                        win[i + 1].get(e), win[i + 2].get(e), win[i + 3].get(e));
-                s[e] = silu_fast(acc);
-                ss = fmaf(s[e], s[e], ss);
-            }
-            ss = row_sum16(ss);
-            const float sc = is_v ? 1.0f : rsqrt_fast(ss + d.eps);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] *= sc;
-            if (active) store8(dst + (s0 + tau0 + i) * stride, s);
+        for (int e = 0; e < 8; ++e) {
+            const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], win[i].get(e),
+                                    win[i + 1].get(e), win[i + 2].get(e), win[i + 3].get(e));
+            s[e] = silu_fast(acc);
+            ss = fmaf(s[e], s[e], ss);
         }
+        ss = row_sum16(ss);
+        const float sc = is_v ? 1.0f : rsqrt_fast(ss + d.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] *= sc;
+        if (active) store8_split_nt(dst + (s0 + t0 + i) * stride, s);
+    };
+    if (nt == TW) {
+#pragma unroll
+        for (int i = 0; i < TW; ++i) token(i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+            if (i < nt) token(i);  // uniform across the wave
     }
 
-    // ---- history carry (tile 0 only; see header) ------------------------
-    if (tile == 0 && active) {
+    // ---- history carry (the sequence's first wave only; see header) -----
+    if (t0 == 0 && active) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
             const int64_t xi = T_n + r;  // row of X that becomes history row r
@@ -143,13 +186,13 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
             if (xi == 0) v = win[0];
             else if (xi == 1) v = win[1];
             else if (xi == 2) v = win[2];
-            else v.load(qkv + (s0 + xi - 3) * C + c0);
-            v.store(hist + ((int64_t)n * 3 + r) * C + c0);
+            else v.load_split(qkv + (s0 + xi - 3) * C + c0);
+            v.store_split(hist + ((int64_t)n * 3 + r) * C + c0);
         }
     }
 }
 
-template <typename TI, int TT>
+template <typename TI, int TW>
 static hipError_t launch_pre_t(const gdn_shape &s, const PreArgs &a, hipStream_t st)
 {
     PreDims d;
@@ -158,17 +201,17 @@ static hipError_t launch_pre_t(const gdn_shape &s, const PreArgs &a, hipStream_t
     d.C = 2 * s.hk * 128 + s.hv * 128;
     d.U = d.C / 128;
     d.n_ug = (d.U + 3) / 4;
-    d.tiles_per_seq = (int)((s.max_T + TT - 1) / TT);
+    d.tiles_per_seq = (int)((s.max_T + 4 * TW - 1) / (4 * TW));
     d.eps = s.eps_l2;
-    const dim3 grid((unsigned)(s.n_seq * (int64_t)d.tiles_per_seq), (unsigned)((d.n_ug + 1 + 3) / 4));
-    hipLaunchKernelGGL((pre_kernel<TI, TT>), grid, dim3(256), 0, st, a, d);
+    const dim3 grid((unsigned)(s.n_seq * (int64_t)d.tiles_per_seq), (unsigned)(d.n_ug + 1));
+    hipLaunchKernelGGL((pre_kernel<TI, TW>), grid, dim3(256), 0, st, a, d);
     return hipGetLastError();
 }
 
 hipError_t launch_pre(const gdn_shape &s, const PreArgs &a, hipStream_t st)
 {
-    if (s.io_dtype == GDN_F16) return launch_pre_t<_Float16, PRE_TILE_F16>(s, a, st);
-    return launch_pre_t<float, PRE_TILE_F32>(s, a, st);
+    if (s.io_dtype == GDN_F16) return launch_pre_t<_Float16, PRE_WAVE_TOKENS>(s, a, st);
+    return launch_pre_t<float, PRE_WAVE_TOKENS>(s, a, st);
 }
 
 } // namespace gdn

@@ -61,7 +61,10 @@
 //   chunks ahead (four LDS copies).  An output wave forms O = Lam R + M U
 //   (1 + 1 products per row group) one step behind, from the partial Q S^T,
 //   U, Lam and M the compute waves leave in LDS, so the outputs stay off the
-//   recurrence's path.
+//   recurrence's path.  In the layer path with fp16 inputs a v wave forms v
+//   of the block's channels from the raw qkv rows the copy wave brings (conv
+//   with the history, SiLU: the pre stage's expressions) and carries their
+//   history, so the fp32 v never goes through memory.
 // * Block order is XCD-aware: blocks are dealt round-robin to the 8 XCDs, so
 //   the index is permuted to give each XCD whole key-head groups, whose
 //   key-head slots are then shared in one L2.
@@ -442,16 +445,13 @@ struct ChunkDims {
 // of 16 channels, and each row group is shared by a pair of waves, one per half
 // of the 128 keys; each of these four compute waves holds its 16 x 64 quarter
 // of the block's state.  A fifth wave only copies operands into LDS, and a
-// sixth forms the outputs from what the compute waves leave in LDS.
+// sixth forms the outputs from what the compute waves leave in LDS.  With
+// RAW_V a seventh wave forms v of the block's channels from the raw fp16 qkv
+// rows (conv with the history, SiLU) instead of the copy wave bringing vc.
 constexpr int CHUNK_WAVES = 4;                       // compute waves: 2 row groups x 2 key halves
-constexpr int CHUNK_THREADS = 64 * (CHUNK_WAVES + 2); // + the copy wave and the output wave
+constexpr int chunk_threads(bool raw_v) { return 64 * (CHUNK_WAVES + 2 + (raw_v ? 1 : 0)); }
 constexpr int CHUNK_ROWS = 32;                       // value channels per block
 constexpr int NBUF = 4;                              // LDS copies of a chunk's operands
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wave are outstanding (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt
-// left at their maximum, i.e. not waited for).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Block-wide barrier ordering LDS only: global copies in flight stay in flight.
 __device__ __forceinline__ void lds_barrier()
@@ -475,12 +475,19 @@ __device__ __forceinline__ void side_barrier()
     __asm__ volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, ChunkDims d)
+template <bool RAW_V>
+__global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanArgs p, ChunkDims d,
+                                                                         VRawArgs vr)
 {
     // operands of four chunks in flight: key-head slot, value-head slot, v
     __shared__ __attribute__((aligned(16))) float sKH[NBUF][SCAN_KH_FLOATS];
     __shared__ __attribute__((aligned(16))) float sVH[NBUF][SCAN_SLOT_FLOATS];
     __shared__ __attribute__((aligned(16))) float sV[NBUF][CT][CHUNK_ROWS];
+    // RAW_V: raw fp16 qkv rows of the block's value channels, per chunk, and
+    // the old history rows of those channels
+    constexpr int RAW_BUF = RAW_V ? NBUF : 1;
+    __shared__ __attribute__((aligned(16))) _Float16 sRaw[RAW_BUF][CT][CHUNK_ROWS];
+    __shared__ __attribute__((aligned(16))) _Float16 sRawH[3][CHUNK_ROWS];
     // partial K S^T and Q S^T of every compute wave, and U of each row group
     __shared__ __attribute__((aligned(16))) f4 sXP[2][CHUNK_WAVES][64];
     __shared__ __attribute__((aligned(16))) f4 sXR[2][CHUNK_WAVES][64];
@@ -522,10 +529,13 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         constexpr int VH_PIECES = (SCAN_SLOT_FLOATS * 4 + 1023) / 1024;             // 3
         // the last value-head piece is 256 bytes: one dword per lane
         static_assert(SCAN_SLOT_FLOATS * 4 - (VH_PIECES - 1) * 1024 == 256, "value-head tail");
-        constexpr int V_PIECES = CT * CHUNK_ROWS * 4 / 1024;                        // 2
+        // v: 2 copies of vc, or (RAW_V) 1 copy of the raw fp16 rows, which the
+        // v wave turns into v
+        constexpr int V_PIECES = RAW_V ? 1 : CT * CHUNK_ROWS * 4 / 1024;
         constexpr int V_LANES = CHUNK_ROWS / 4;                                     // lanes per token
         constexpr int PER_CHUNK = KH_PIECES + VH_PIECES + V_PIECES;                 // copies per chunk
-        static_assert(V_PIECES * 1024 == CT * CHUNK_ROWS * 4, "v pieces");
+        static_assert(RAW_V ? CT * CHUNK_ROWS * 2 == 1024 : V_PIECES * 1024 == CT * CHUNK_ROWS * 4,
+                      "v pieces");
         static_assert(2 * PER_CHUNK <= 63, "vmcnt range");
         auto copy16 = [](const float *src, float *lds_piece) {
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_piece, 16, 0, 0);
@@ -548,11 +558,20 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
 #pragma unroll
             for (int m = 0; m < VH_PIECES - 1; ++m) copy16(vhs + m * 256 + lane * 4, &sVH[b][m * 256]);
             copy4(vhs + (VH_PIECES - 1) * 256 + lane, &sVH[b][(VH_PIECES - 1) * 256]);
-            const float *vb = p.vc + (tb * hv + h) * 128 + rb * CHUNK_ROWS + (lane % V_LANES) * 4;
+            if constexpr (RAW_V) {
+                // lane l: token l / 4, raw channels 8 (l % 4) .. + 7 of the block's
+                // 32, landing at sRaw[b][l / 4][8 (l % 4)]
+                const _Float16 *src = static_cast<const _Float16 *>(vr.qkv) +
+                                      (tb + min(lane >> 2, nv - 1)) * vr.C + (2 * hk + h) * 128 +
+                                      rb * CHUNK_ROWS + (lane & 3) * 8;
+                __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)&sRaw[b][0][0], 16, 0, 0);
+            } else {
+                const float *vb = p.vc + (tb * hv + h) * 128 + rb * CHUNK_ROWS + (lane % V_LANES) * 4;
 #pragma unroll
-            for (int m = 0; m < V_PIECES; ++m) {
-                const int t = m * (64 / V_LANES) + lane / V_LANES;
-                copy16(vb + (uint32_t)min(t, nv - 1) * vstride, &sV[b][m * (64 / V_LANES)][0]);
+                for (int m = 0; m < V_PIECES; ++m) {
+                    const int t = m * (64 / V_LANES) + lane / V_LANES;
+                    copy16(vb + (uint32_t)min(t, nv - 1) * vstride, &sV[b][m * (64 / V_LANES)][0]);
+                }
             }
         };
         // Chunk c sits in LDS copy c % 4.  It is issued after the barrier of
@@ -613,6 +632,79 @@ __global__ __launch_bounds__(CHUNK_THREADS) void scan_chunk_kernel(ScanArgs p, C
         side_barrier();
         o_store(n_chunks - 1);
         return;
+    }
+
+    if constexpr (RAW_V) {
+        if (wave == CHUNK_WAVES + 2) {
+            // ---- v wave: v of chunk c between the barriers of steps c - 1 and
+            // c (the first: the initial barrier), into sV, from the raw rows the
+            // copy wave brings with the chunk's other operands (in LDS from the
+            // barrier of step c - 1 on).  Lane l takes token l / 4 of the chunk
+            // and value channels 8 (l % 4) .. + 7 of the block's 32.  The
+            // arithmetic is gdn_pre's (conv4, silu_fast), so v is bit for bit
+            // the staged path's.
+            const _Float16 *qkv = static_cast<const _Float16 *>(vr.qkv);
+            const _Float16 *cw = static_cast<const _Float16 *>(vr.conv_w);
+            _Float16 *hist = static_cast<_Float16 *>(vr.hist) + (int64_t)n * 3 * vr.C;
+            const int C = vr.C;
+            const int cv = (2 * hk + h) * 128 + rb * CHUNK_ROWS;  // the block's first raw channel
+            const int t = lane >> 2, g8 = (lane & 3) * 8;
+            float w[8][4];
+            {
+                float tw[4][8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) load8(cw + (int64_t)(cv + g8) * 4 + k * 8, tw[k]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = tw[k][e];
+            }
+            // the old history rows of the block's channels (lanes 0..11)
+            Raw8<_Float16> hrow;
+            if (lane < 12) hrow.load(hist + (int64_t)(lane >> 2) * C + cv + g8);
+            wait_vmem_all();
+            if (lane < 12) *reinterpret_cast<h8 *>(&sRawH[lane >> 2][g8]) = hrow.v;
+            // taps of token t: raw rows t - 3 .. t, reaching into the previous
+            // chunk's rows (or the history, for chunk 0)
+            auto conv_chunk = [&](int c) {
+                const int b = c & (NBUF - 1), pb = (c - 1) & (NBUF - 1), rbuf = b;
+                Raw8<_Float16> x[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int r = t + m - 3;
+                    const _Float16 *rp = r >= 0 ? &sRaw[rbuf][r][g8]
+                                       : c == 0 ? &sRawH[3 + r][g8] : &sRaw[pb][CT + r][g8];
+                    x[m].v = *reinterpret_cast<const h8 *>(rp);
+                }
+                f4 s0, s1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float acc = conv4(w[e][0], w[e][1], w[e][2], w[e][3], x[0].get(e), x[1].get(e),
+                                            x[2].get(e), x[3].get(e));
+                    (e < 4 ? s0 : s1)[e & 3] = silu_fast(acc);
+                }
+                *reinterpret_cast<f4 *>(&sV[b][t][g8]) = s0;
+                *reinterpret_cast<f4 *>(&sV[b][t][g8 + 4]) = s1;
+            };
+            side_barrier();
+            conv_chunk(0);
+            for (int c = 0; c < n_chunks; ++c) {
+                side_barrier();
+                if (c + 1 < n_chunks) conv_chunk(c + 1);
+            }
+            side_barrier();
+            // the new history of the block's channels: X rows T_n .. T_n + 2 of
+            // X = [old history; the sequence's rows]
+            if (lane < 12) {
+                const int r = lane >> 2;
+                const int64_t xi = (int64_t)T_n + r;
+                Raw8<_Float16> v;
+                if (xi < 3) v.v = *reinterpret_cast<const h8 *>(&sRawH[xi][g8]);
+                else v.load(qkv + ((int64_t)cu0 + xi - 3) * C + cv + g8);
+                v.store(hist + (int64_t)r * C + cv + g8);
+            }
+            return;
+        }
     }
 
     // ---- compute waves ---------------------------------------------------
@@ -746,7 +838,7 @@ static int64_t scan_slots(const gdn_shape &s)
 // the staged path's bit for bit.  History carry without a race: only the
 // chunk-0 blocks read the old history, each for its own channels, and the
 // same block writes the new history of those channels after a barrier.
-template <typename TI>
+template <typename TI, bool RAW_V>
 __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDims d)
 {
     __shared__ __attribute__((aligned(16))) PrepShared sm;
@@ -766,45 +858,53 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
     const TI *qkv = static_cast<const TI *>(p.qkv);
     const TI *cw = static_cast<const TI *>(p.conv_w);
     TI *hist = static_cast<TI *>(p.hist) + (int64_t)n * 3 * C;
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    // Tasks (unit u, half hf) of 8 tokens x 128 channels, one per 16-lane row,
-    // 8 channels per lane: u = 0 q of key head j, u = 1 its k, u = 2 + gh v of
-    // value head j G + gh.  A task loads its weights once and its 11 rows of
-    // X up front, then walks the 8 tokens.
-    const int units = 2 + G;
+    // Tasks (unit u, token part) of up to 8 tokens x 128 channels, one per
+    // 16-lane row: u = 0 q of key head j, u = 1 its k, u = 2 + gh v of value
+    // head j G + gh.  Each unit's 16 tokens are cut into P parts, P as large as
+    // keeps the units x P tasks within the block's 16 rows (production: 5
+    // units x 3 parts of 5, 5 and 6 tokens on 15 rows).  Lane l16 of the row
+    // takes channels 4 l16 .. + 3 and 64 + 4 l16 .. + 3 of the unit (every
+    // memory instruction covers whole 64-channel runs).  A task issues its
+    // weight loads and the rows of X its tokens read, all unconditional (rows
+    // past the chunk's end repeat its last row), waits for them once, and then
+    // walks its tokens with no load behind a store.
+    const int units = RAW_V ? 2 : 2 + G;  // RAW_V: v is the chunk kernel's
+    const int P = units > 8 ? 2 : CT / units;
     auto unit_base = [&](int u) {
         return u == 0 ? j * 128 : u == 1 ? (hk + j) * 128 : (2 * hk + j * G + (u - 2)) * 128;
     };
     // row xi of X = [history (3 rows); the sequence's tokens]
-    auto xrow = [&](int64_t xi, int ch, Raw8<TI> &x) {
-        if (xi < 3) x.load(hist + xi * C + ch);
-        else x.load(qkv + (cu0 + xi - 3) * C + ch);
+    auto xrow_ptr = [&](int64_t xi, int ch) {
+        return xi < 3 ? hist + xi * C + ch : qkv + (cu0 + xi - 3) * C + ch;
     };
-    const int ntask = 2 * units;
+    const int ntask = units * P;
     for (int task = wave * 4 + (lane >> 4); task < ntask; task += 16) {  // uniform per 16-lane row
-        const int u = task >> 1, hf = task & 1;
-        const int ch = unit_base(u) + l16 * 8;
-        const int t0 = 8 * hf;
-        const int nt = max(0, min(8, nv - t0));  // valid tokens of this task
+        const int u = task / P, part = task - u * P;
+        const int ch = unit_base(u) + l16 * 4;
+        const int t0 = CT * part / P;
+        const int ntok = CT * (part + 1) / P - t0;  // tokens of this task (at most 8)
+        const int nt = max(0, min(ntok, nv - t0));  // valid ones
         float w[8][4];
         {
-            float tw[8];
+            float tw[4][8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                load8(cw + (int64_t)ch * 4 + k * 8, tw);
+            for (int k = 0; k < 4; ++k) load8(cw + (int64_t)(ch + 64 * (k >> 1)) * 4 + (k & 1) * 8, tw[k]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = tw[e];
-            }
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[(k * 8 + e) >> 2][(k * 8 + e) & 3] = tw[k][e];
         }
-        const int64_t xb = (int64_t)c * CT + t0;  // X row of tap 0 of the first token
+        const int64_t xb = (int64_t)c * CT + t0;          // X row of tap 0 of the first token
+        const int64_t x_last = (int64_t)c * CT + nv + 2;  // tap 3 of the chunk's last token
         Raw8<TI> x[11];
 #pragma unroll
-        for (int i = 0; i < 11; ++i) {
-            if (i < nt + 3) xrow(xb + i, ch, x[i]);
-            else x[i].zero();
-        }
+        for (int i = 0; i < 11; ++i) x[i].load_split(xrow_ptr(min(xb + min(i, ntok + 2), x_last), ch));
+        wait_vmem_all();
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            if (i >= ntok) break;  // uniform per 16-lane row
             const int t = t0 + i;
             float sv[8];
             float ss = 0.f;
@@ -818,11 +918,13 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
             if (u < 2) {
                 ss = row_sum16(ss);
                 const float sc = rsqrt_fast(ss + d.eps_l2);
-                float *dst = u == 0 ? &sm.sQ[t][l16 * 8] : &sm.sK[t][l16 * 8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dst[e] = i < nt ? sv[e] * sc : 0.f;
+                float *dst = u == 0 ? &sm.sQ[t][l16 * 4] : &sm.sK[t][l16 * 4];
+                *reinterpret_cast<f4 *>(dst) =
+                    i < nt ? f4{sv[0] * sc, sv[1] * sc, sv[2] * sc, sv[3] * sc} : z4;
+                *reinterpret_cast<f4 *>(dst + 64) =
+                    i < nt ? f4{sv[4] * sc, sv[5] * sc, sv[6] * sc, sv[7] * sc} : z4;
             } else if (i < nt) {
-                store8(p.vc + ((tb + t) * hv + j * G + (u - 2)) * 128 + l16 * 8, sv);
+                store8_split_nt(p.vc + ((tb + t) * hv + j * G + (u - 2)) * 128 + l16 * 4, sv);
             }
         }
     }
@@ -847,15 +949,15 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
 
     // the new history of this block's channels (chunk 0 only)
     if (c == 0 && tid < units * 16) {
-        const int ch = unit_base(tid >> 4) + l16 * 8;
+        const int ch = unit_base(tid >> 4) + l16 * 4;
+        Raw8<TI> v[3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            // X row T_n + r; for T_n + r < 3 it is old history row T_n + r > r,
-            // not yet overwritten
-            Raw8<TI> v;
-            xrow((int64_t)T_n + r, ch, v);
-            v.store(hist + (int64_t)r * C + ch);
-        }
+        for (int r = 0; r < 3; ++r) v[r].load_split(xrow_ptr((int64_t)T_n + r, ch));
+        // X row T_n + r; for T_n + r < 3 it is old history row T_n + r > r,
+        // not yet overwritten: all three are read before the first write
+        wait_vmem_all();
+#pragma unroll
+        for (int r = 0; r < 3; ++r) v[r].store_split(hist + (int64_t)r * C + ch);
     }
 
     auto load_gb = [&](int gh, float &gl, float &bl) {
@@ -881,7 +983,8 @@ static PrepDims prep_dims(const gdn_shape &s)
     return pd;
 }
 
-static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
+static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_t st,
+                               const VRawArgs *vr = nullptr)
 {
     ChunkDims cd;
     cd.hk = s.hk;
@@ -890,7 +993,12 @@ static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_
     cd.vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
     cd.m1 = -1.f;
     const int64_t blocks = (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS);
-    hipLaunchKernelGGL(scan_chunk_kernel, dim3((unsigned)blocks), dim3(CHUNK_THREADS), 0, st, a, cd);
+    if (vr)
+        hipLaunchKernelGGL(scan_chunk_kernel<true>, dim3((unsigned)blocks), dim3(chunk_threads(true)), 0,
+                           st, a, cd, *vr);
+    else
+        hipLaunchKernelGGL(scan_chunk_kernel<false>, dim3((unsigned)blocks), dim3(chunk_threads(false)), 0,
+                           st, a, cd, VRawArgs{});
     return hipGetLastError();
 }
 
@@ -909,10 +1017,15 @@ hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const 
 {
     const PrepDims pd = prep_dims(s);
     const dim3 grid((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk);
-    if (s.io_dtype == GDN_F16)
-        hipLaunchKernelGGL(layer_prep_kernel<_Float16>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
-    else
-        hipLaunchKernelGGL(layer_prep_kernel<float>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+    if (s.io_dtype == GDN_F16) {
+        // v of the value heads is formed in the chunk kernel (VRawArgs)
+        hipLaunchKernelGGL((layer_prep_kernel<_Float16, true>), grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const VRawArgs vr{lp.qkv, lp.conv_w, lp.hist, pd.C};
+        return launch_chunk(s, a, st, &vr);
+    }
+    hipLaunchKernelGGL((layer_prep_kernel<float, false>), grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_chunk(s, a, st);
