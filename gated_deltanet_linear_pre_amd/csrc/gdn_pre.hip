@@ -42,13 +42,17 @@ namespace gdn {
 
 struct PreDims {
     int hk, hv, C, U;          // U = C / 128 head units
-    int n_ug;                  // unit groups of 4 (blockIdx.y of the conv blocks)
+    int n_ug;                  // unit groups of 4 (blockIdx.x of the conv blocks)
     int tiles_per_seq;
+    int64_t n_tiles;           // n_seq x tiles_per_seq (grid y and z)
     float eps;
 };
 
-// One block per (tile of 4 TW tokens, unit group of 4 units); wave w takes the
-// tile's tokens w TW .. w TW + TW - 1.  blockIdx.y == n_ug: the tile's gates.
+// One block per (unit group of 4 units, tile of 4 TW tokens); wave w takes the
+// tile's tokens w TW .. w TW + TW - 1.  blockIdx.x == n_ug: the tile's gates.
+// The unit group is the fast grid index, so the blocks resident at one time
+// read whole token rows (measured: 25.5 us per production layer, against 28.1
+// with the tile as the fast index, and 27.4 with runs of tiles kept on one XCD).
 template <typename TI, int TW>
 __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
 {
@@ -57,10 +61,10 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    // consecutive tiles of one unit group on one XCD (blocks go round-robin
-    // over the 8 XCDs), so a tile's 3-row halo is mostly an L2 hit
-    int bx = blockIdx.x;
-    if ((gridDim.x & 7) == 0) bx = (bx & 7) * (gridDim.x >> 3) + (bx >> 3);
+    // tile index over grid y and z (grid y holds at most 65535 blocks)
+    const int64_t bxl = (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+    if (bxl >= d.n_tiles) return;
+    const int bx = (int)bxl;
     const int n = bx / d.tiles_per_seq;
     const int tile = bx - n * d.tiles_per_seq;
     const int64_t s0 = p.cu[n];
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
     const int64_t tau0 = (int64_t)tile * TT;
     if (tau0 >= T_n) return;
 
-    if ((int)blockIdx.y == d.n_ug) {
+    if ((int)blockIdx.x == d.n_ug) {
         // ---- gates of the tile's tokens, GB per thread per round; every
         // load of a round is issued before the round's first store
         constexpr int GB = 4;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void pre_kernel(PreArgs p, PreDims d)
     const TI *cw = static_cast<const TI *>(p.conv_w);
     TI *hist = static_cast<TI *>(p.hist);
     const int C = d.C;
-    const int u = (int)blockIdx.y * 4 + (lane >> 4);
+    const int u = (int)blockIdx.x * 4 + (lane >> 4);
     const int l16 = lane & 15;
     const bool active = u < d.U;
     // lane l16 of the row owns channels 4 l16 .. + 3 (values 0..3) and
@@ -202,8 +206,12 @@ static hipError_t launch_pre_t(const gdn_shape &s, const PreArgs &a, hipStream_t
     d.U = d.C / 128;
     d.n_ug = (d.U + 3) / 4;
     d.tiles_per_seq = (int)((s.max_T + 4 * TW - 1) / (4 * TW));
+    d.n_tiles = (int64_t)s.n_seq * d.tiles_per_seq;
     d.eps = s.eps_l2;
-    const dim3 grid((unsigned)(s.n_seq * (int64_t)d.tiles_per_seq), (unsigned)(d.n_ug + 1));
+    if (d.n_tiles == 0) return hipSuccess;
+    const unsigned gy = (unsigned)(d.n_tiles < 65535 ? d.n_tiles : 65535);
+    const unsigned gz = (unsigned)((d.n_tiles + gy - 1) / gy);
+    const dim3 grid((unsigned)(d.n_ug + 1), gy, gz);
     hipLaunchKernelGGL((pre_kernel<TI, TW>), grid, dim3(256), 0, st, a, d);
     return hipGetLastError();
 }
