@@ -17,16 +17,21 @@
 // gfx950 mapping.  Decode moves the whole state (64 KB per head) in and out
 // for 7 flop per element, so it is bound by HBM bandwidth and launch latency.
 // One 256-thread block per (sequence, value head):
-//   - each thread issues the loads of its 64 state elements (row r = t / 2,
-//     key half t % 2, sixteen 16-byte loads) first, so they are in flight
-//     while the block computes the token's q, k, v and gates;
+//   - each thread issues the loads of its 64 state elements first, so they
+//     are in flight while the block computes the token's q, k, v and gates.
+//     A group of 8 lanes owns 4 rows; in each of its 16 loads (and stores)
+//     the group covers one whole 128-byte line (32 keys) of one row, lane e
+//     taking keys 4e..4e+3 of it, so every memory instruction moves whole
+//     lines (with half a row per thread each instruction touched 64 lines,
+//     16 bytes of each);
 //   - threads 0..127 each take channel c of the key head's q and k and of the
 //     value head's v: 4-tap conv, SiLU, and the three sums q.q, k.k, q.k,
 //     reduced over the block (DPP inside a 16-lane row, then LDS);
-//   - the state step: each thread forms its half-row dot products S k^ and
-//     S q^ over 64 keys, adds its neighbour lane's half (the pair sums in one
-//     order), and writes alpha S + u k^T back; o = alpha (S q^) + u (k^.q^)
-//     is the same quantity as (alpha S + u k^T) q^ in one pass;
+//   - the state step: each thread forms its 16-key parts of S k^ and S q^
+//     for its 4 rows, the group adds them in a 3-step butterfly (every lane
+//     ends with the same bits), and writes alpha S + u k^T back;
+//     o = alpha (S q^) + u (k^.q^) is the same quantity as (alpha S + u k^T) q^
+//     in one pass;
 //   - the RMSNorm over the head's 128 outputs and the gated output.
 // A second launch shifts the history (every block of a key-head group reads
 // the group's q/k history, so no block of the first launch may overwrite it).
@@ -58,7 +63,6 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p, StepDims d)
 {
     __shared__ float sq[128], sk[128], sv[128];
     __shared__ float red[4][4];
-    __shared__ float gates[2];
     __shared__ float orow[128];
 
     const int tid = threadIdx.x;
@@ -68,30 +72,58 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p, StepDims d)
     const int j = h / d.G;
     const int C = d.C;
 
-    // ---- issue the state loads first ---------------------------------------
-    const int r = tid >> 1, kh = tid & 1;
-    float *Srow = p.state + (((int64_t)n * d.hv + h) * 128 + r) * 128 + 64 * kh;
-    float4 S[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = reinterpret_cast<const float4 *>(Srow)[i];
-
-    // ---- the token's q, k (key head j) and v (value head h) ---------------
+    // ---- the token's inputs, then the state -------------------------------
+    // Every thread loads the inputs of channel tid % 128 of the key head's q
+    // and k and of the value head's v, and the head's gate inputs (the same
+    // for all), unconditionally and before the state: loads complete in
+    // order, so the conv and the norms below wait only for these, while the
+    // state's 64 KB is still on its way.
     const TI *qkv = static_cast<const TI *>(p.qkv) + (int64_t)n * C;
     const TI *hist = static_cast<const TI *>(p.hist) + (int64_t)n * 3 * C;
     const TI *cw = static_cast<const TI *>(p.conv_w);
+    const int c = tid & 127;
+    const int chq = j * 128 + c, chk = d.hk * 128 + j * 128 + c, chv = 2 * d.hk * 128 + h * 128 + c;
+    // raw values first (converted only once the state loads are out)
+    TI wq[4], wk[4], wv[4], xq[4], xk[4], xv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        wq[m] = cw[(int64_t)chq * 4 + m];
+        wk[m] = cw[(int64_t)chk * 4 + m];
+        wv[m] = cw[(int64_t)chv * 4 + m];
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        xq[m] = hist[m * C + chq];
+        xk[m] = hist[m * C + chk];
+        xv[m] = hist[m * C + chv];
+    }
+    xq[3] = qkv[chq];
+    xk[3] = qkv[chk];
+    xv[3] = qkv[chv];
+    const TI ga = static_cast<const TI *>(p.a)[(int64_t)n * d.hv + h];
+    const TI gb = static_cast<const TI *>(p.b)[(int64_t)n * d.hv + h];
+    const TI gdt = static_cast<const TI *>(p.dt_bias)[h];
+    const TI gal = static_cast<const TI *>(p.A_log)[h];
+
+    // S[4 m + l] = keys 32 l + 4 e .. + 3 of row 4 grp + m
+    const int grp = tid >> 3, e = tid & 7;
+    float *Sblk = p.state + (((int64_t)n * d.hv + h) * 128 + 4 * grp) * 128 + 4 * e;
+    float4 S[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        S[i] = *reinterpret_cast<const float4 *>(Sblk + (i >> 2) * 128 + (i & 3) * 32);
+    __builtin_amdgcn_sched_barrier(0);  // every load is out before the first use
+
+    // ---- the token's q, k (key head j) and v (value head h) ---------------
+    auto cv4 = [](const TI (&w)[4], const TI (&x)[4]) {
+        return silu_fast(conv4((float)w[0], (float)w[1], (float)w[2], (float)w[3], (float)x[0],
+                               (float)x[1], (float)x[2], (float)x[3]));
+    };
+    const float q = cv4(wq, xq);
+    const float k = cv4(wk, xk);
+    const float v = cv4(wv, xv);
     float sumq = 0.f, sumk = 0.f, sumqk = 0.f;
     if (tid < 128) {
-        const int c = tid;
-        auto conv_silu = [&](int ch) {
-            float acc = ld1(cw + (int64_t)ch * 4 + 0) * ld1(hist + ch);
-            acc = fmaf(ld1(cw + (int64_t)ch * 4 + 1), ld1(hist + C + ch), acc);
-            acc = fmaf(ld1(cw + (int64_t)ch * 4 + 2), ld1(hist + 2 * C + ch), acc);
-            acc = fmaf(ld1(cw + (int64_t)ch * 4 + 3), ld1(qkv + ch), acc);
-            return silu_fast(acc);
-        };
-        const float q = conv_silu(j * 128 + c);
-        const float k = conv_silu(d.hk * 128 + j * 128 + c);
-        const float v = conv_silu(2 * d.hk * 128 + h * 128 + c);
         sq[c] = q;
         sk[c] = k;
         sv[c] = v;
@@ -109,52 +141,59 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p, StepDims d)
             red[wave][2] = sumqk;
         }
     }
-    if (tid == 0) {
-        const TI *a = static_cast<const TI *>(p.a);
-        const TI *b = static_cast<const TI *>(p.b);
-        const float x = ld1(a + (int64_t)n * d.hv + h) + ld1(static_cast<const TI *>(p.dt_bias) + h);
-        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-        const float g = -expf(ld1(static_cast<const TI *>(p.A_log) + h)) * sp;
-        gates[0] = expf(g);
-        gates[1] = 1.0f / (1.0f + expf(-ld1(b + (int64_t)n * d.hv + h)));
-    }
+    // the gates, formed by every thread from the same inputs in the same way
+    float g, beta;
+    gates((float)ga, (float)gdt, (float)gal, (float)gb, g, beta);
+    const float alpha = expf(g);
     __syncthreads();
     const float inv_q = rsqrt_fast((red[0][0] + red[1][0]) + d.eps_l2);
     const float inv_k = rsqrt_fast((red[0][1] + red[1][1]) + d.eps_l2);
     const float kq = (red[0][2] + red[1][2]) * inv_q * inv_k;
-    const float alpha = gates[0], beta = gates[1];
 
-    // ---- one step of the delta rule on this thread's half row --------------
-    float Sk = 0.f, Sq = 0.f;
+    // ---- one step of the delta rule on this thread's 4 row pieces -----------
+    float4 kv[4], qv[4];  // keys 32 l + 4 e .. + 3
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 kv = *reinterpret_cast<const float4 *>(&sk[64 * kh + 4 * i]);
-        const float4 qv = *reinterpret_cast<const float4 *>(&sq[64 * kh + 4 * i]);
-        Sk = fmaf(S[i].x, kv.x, Sk); Sk = fmaf(S[i].y, kv.y, Sk);
-        Sk = fmaf(S[i].z, kv.z, Sk); Sk = fmaf(S[i].w, kv.w, Sk);
-        Sq = fmaf(S[i].x, qv.x, Sq); Sq = fmaf(S[i].y, qv.y, Sq);
-        Sq = fmaf(S[i].z, qv.z, Sq); Sq = fmaf(S[i].w, qv.w, Sq);
+    for (int l = 0; l < 4; ++l) {
+        kv[l] = *reinterpret_cast<const float4 *>(&sk[32 * l + 4 * e]);
+        qv[l] = *reinterpret_cast<const float4 *>(&sq[32 * l + 4 * e]);
     }
-    // the key halves of a row sit in neighbouring lanes; both add them in
-    // the order (lower keys) + (upper keys)
-    const float Sk_o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Sk), 0xB1, 0xF, 0xF, false));
-    const float Sq_o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Sq), 0xB1, 0xF, 0xF, false));
-    const float Skf = (kh == 0 ? Sk + Sk_o : Sk_o + Sk) * inv_k;
-    const float Sqf = (kh == 0 ? Sq + Sq_o : Sq_o + Sq) * inv_q;
-    const float u = beta * (sv[r] - alpha * Skf);
-    const float uk = u * inv_k;
+    // the sum over the 8 lanes of the group: lanes exchange with lane ^ 1,
+    // lane ^ 2 (quad permutes) and 7 - lane (half-row mirror); each addition
+    // pairs equal partial sums, so every lane gets the same bits
+    auto group_sum = [](float x) {
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+        x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+        return x;
+    };
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float4 kv = *reinterpret_cast<const float4 *>(&sk[64 * kh + 4 * i]);
-        float4 x;
-        x.x = fmaf(uk, kv.x, alpha * S[i].x);
-        x.y = fmaf(uk, kv.y, alpha * S[i].y);
-        x.z = fmaf(uk, kv.z, alpha * S[i].z);
-        x.w = fmaf(uk, kv.w, alpha * S[i].w);
-        reinterpret_cast<float4 *>(Srow)[i] = x;
+    for (int m = 0; m < 4; ++m) {
+        float Sk = 0.f, Sq = 0.f;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            const float4 s4 = S[4 * m + l];
+            Sk = fmaf(s4.x, kv[l].x, Sk); Sk = fmaf(s4.y, kv[l].y, Sk);
+            Sk = fmaf(s4.z, kv[l].z, Sk); Sk = fmaf(s4.w, kv[l].w, Sk);
+            Sq = fmaf(s4.x, qv[l].x, Sq); Sq = fmaf(s4.y, qv[l].y, Sq);
+            Sq = fmaf(s4.z, qv[l].z, Sq); Sq = fmaf(s4.w, qv[l].w, Sq);
+        }
+        const float Skf = group_sum(Sk) * inv_k;
+        const float Sqf = group_sum(Sq) * inv_q;
+        const int r = 4 * grp + m;
+        const float u = beta * (sv[r] - alpha * Skf);
+        const float uk = u * inv_k;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            const float4 s4 = S[4 * m + l];
+            float4 x;
+            x.x = fmaf(uk, kv[l].x, alpha * s4.x);
+            x.y = fmaf(uk, kv[l].y, alpha * s4.y);
+            x.z = fmaf(uk, kv[l].z, alpha * s4.z);
+            x.w = fmaf(uk, kv[l].w, alpha * s4.w);
+            *reinterpret_cast<float4 *>(Sblk + m * 128 + l * 32) = x;
+        }
+        if (e == 0) orow[r] = (alpha * Sqf + u * kq) * STEP_SCALE;
     }
-    const float o = (alpha * Sqf + u * kq) * STEP_SCALE;
-    if (kh == 0) orow[r] = o;
     __syncthreads();
 
     // ---- RMSNorm over the head's 128 outputs, gamma, SiLU(z) --------------
