@@ -125,6 +125,41 @@ __device__ __forceinline__ void store8_split_nt(float *__restrict__ p, const flo
     __builtin_nontemporal_store(b, reinterpret_cast<v4 *>(p + 64));
 }
 
+// the split channel mapping for whole rows: x[0..3] from p[0..3], x[4..7]
+// from p[64..67] (and back)
+__device__ __forceinline__ void load8_split(const float *__restrict__ p, float (&x)[8])
+{
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p + 64)[0];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void load8_split(const _Float16 *__restrict__ p, float (&x)[8])
+{
+    typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+    const h4v a = *reinterpret_cast<const h4v *>(p);
+    const h4v b = *reinterpret_cast<const h4v *>(p + 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = (float)a[i];
+        x[4 + i] = (float)b[i];
+    }
+}
+
+__device__ __forceinline__ void store8_split(_Float16 *__restrict__ p, const float (&x)[8])
+{
+    typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+    h4v a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = (_Float16)x[i];
+        b[i] = (_Float16)x[4 + i];
+    }
+    *reinterpret_cast<h4v *>(p) = a;
+    *reinterpret_cast<h4v *>(p + 64) = b;
+}
+
 // fp32 -> fp16 conversion rounds to nearest even (the default mode).
 __device__ __forceinline__ void store8(_Float16 *__restrict__ p, const float (&x)[8])
 {

@@ -8,10 +8,11 @@
 //
 // gfx950 mapping.  The stage moves 12 B (fp16 y) or 16 B (fp32 y) per element
 // for about 10 flop, so it is bound by HBM bandwidth.  A 16-lane DPP row owns
-// one row of 128 values, 8 consecutive per lane: o arrives as two 16-byte
-// loads, z (fp16) as one, and a wave covers four rows = 2 KB of o in
-// contiguous 1 KB load instructions.  The sum of squares is a 4-step DPP
-// rotate-add inside the row, with no LDS and no barrier.
+// one row of 128 values: lane l takes values 4l..4l+3 and 64+4l..64+4l+3, so
+// every load and store instruction covers whole 64-value runs of its four
+// rows (whole cache lines; with 8 consecutive values per lane each fp32
+// instruction filled half of every line it touched).  The sum of squares is a
+// 4-step DPP rotate-add inside the row, with no LDS and no barrier.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -27,12 +28,12 @@ __global__ __launch_bounds__(256) void post_kernel(const float *__restrict__ o,
     const int l16 = threadIdx.x & 15;
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     if (row >= n_rows) return;  // whole 16-lane rows leave together
-    const int64_t base = row * 128 + l16 * 8;
+    const int64_t base = row * 128 + l16 * 4;
 
     float x[8], zz[8], gm[8];
-    load8(o + base, x);
-    load8(z + base, zz);
-    load8(gamma + l16 * 8, gm);
+    load8_split(o + base, x);
+    load8_split(z + base, zz);
+    load8_split(gamma + l16 * 4, gm);
 
     float ss = 0.f;
 #pragma unroll
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(256) void post_kernel(const float *__restrict__ o,
         const float gate = silu_fast(zz[i]);
         out[i] = ((x[i] * inv) * gm[i]) * gate;
     }
-    store8(y + base, out);
+    store8_split(y + base, out);
 }
 
 template <typename TI, typename TO>
