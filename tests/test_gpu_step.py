@@ -34,6 +34,10 @@ CASES = [
     ("prod_batch3_fp16in_fp32out", 16, 48, 3, "f16", "f32"),
     ("tiny_batch4_fp32", 2, 6, 4, "f32", "f32"),
     ("tiny_batch1_fp32in_fp16out", 2, 6, 1, "f32", "f16"),
+    # one value head per key head (one 256-thread group per block), and five
+    # (value heads handled three at a time: two rounds)
+    ("g1_batch3_fp16", 4, 4, 3, "f16", "f16"),
+    ("g5_batch2_fp16in_fp32out", 2, 10, 2, "f16", "f32"),
 ]
 
 
