@@ -830,14 +830,16 @@ static int64_t scan_slots(const gdn_shape &s)
 //
 // One block per (chunk, key head j) computes, for the chunk's 16 tokens, the
 // pre stage of exactly the channels the prep step needs: q and k of key head
-// j (conv, SiLU, L2 norm) straight into LDS, v of the group's value heads
-// (conv, SiLU) to the vc buffer the chunk kernel reads, and the group's
-// gates; then it builds the slots like scan_prep_kernel.  The normalised q
-// and k and the gates never go through memory.  The arithmetic is that of
-// gdn_pre (the same per-element expressions), so the layer's results equal
-// the staged path's bit for bit.  History carry without a race: only the
-// chunk-0 blocks read the old history, each for its own channels, and the
-// same block writes the new history of those channels after a barrier.
+// j (conv, SiLU, L2 norm) straight into LDS and the group's gates, and
+// without RAW_V also v of the group's value heads (conv, SiLU) to the vc
+// buffer the chunk kernel reads (with RAW_V the chunk kernel forms v from the
+// raw rows and carries those channels' history); then it builds the slots
+// like scan_prep_kernel.  The normalised q and k and the gates never go
+// through memory.  The arithmetic is that of gdn_pre (the same per-element
+// expressions), so the layer's results equal the staged path's bit for bit.
+// History carry without a race: only the chunk-0 blocks read the old history,
+// each for its own channels, and the same block writes the new history of
+// those channels after a barrier.
 template <typename TI, bool RAW_V>
 __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDims d)
 {
