@@ -160,6 +160,20 @@ __device__ __forceinline__ void store8_split(_Float16 *__restrict__ p, const flo
     *reinterpret_cast<h4v *>(p + 64) = b;
 }
 
+// 16-byte non-temporal load and store, for data one pass touches once
+__device__ __forceinline__ float4 load4_nt(const float *__restrict__ p)
+{
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const v4 t = __builtin_nontemporal_load(reinterpret_cast<const v4 *>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void store4_nt(float *__restrict__ p, float4 x)
+{
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const v4 t = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4 *>(p));
+}
+
 // fp32 -> fp16 conversion rounds to nearest even (the default mode).
 __device__ __forceinline__ void store8(_Float16 *__restrict__ p, const float (&x)[8])
 {
