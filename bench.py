@@ -65,16 +65,17 @@ def kernel_source_hash(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per scan launch from rocprofv3 counters, if they were taken on
-    the scan kernel as it is now (source hash match); else None."""
+def load_counters():
+    """rocprofv3 counter figures of the scan (HBM bytes per launch, MFMA and
+    VALU utilisation), if they were taken on the scan kernel as it is now
+    (source hash match); else {}."""
     try:
         d = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
-        return None
+        return {}
     if d.get("kernel_source_sha256_16") != kernel_source_hash("gdn_scan.hip"):
-        return None
-    return d.get("bytes_per_launch")
+        return {}
+    return d
 
 
 def cpu_baseline(budget_s=15.0, layers_total=36):
@@ -249,7 +250,8 @@ def main():
 
     scan_s = r16["scan_ms"] / 1e3
     achieved_tf = scan_flops(T, hv) / scan_s / 1e12
-    traffic = load_traffic()
+    ctr = load_counters()
+    traffic = ctr.get("bytes_per_launch")
     # achieved = the recurrence's fp32 flops (7 per state element and token) per call / the
     # call's event-timed duration; the contractions execute as three fp16 MFMA products per
     # fp32 product, so the peak is the dense fp16 MFMA figure
@@ -259,7 +261,11 @@ def main():
             "kernel": "gdn_scan (scan_prep_kernel + scan_chunk_kernel), per layer launch",
             "flops_per_launch": scan_flops(T, hv),
             "frac_of_fp32_mfma_peak": round(achieved_tf / FP32_MFMA_PEAK_TFLOPS, 4),
-            "frac_of_split_fp16_peak": round(achieved_tf / (FP16_MFMA_PEAK_TFLOPS / 3), 4)}
+            "frac_of_split_fp16_peak": round(achieved_tf / (FP16_MFMA_PEAK_TFLOPS / 3), 4),
+            # chunk kernel, from the counters: MFMA busy cycles over all SIMD cycles (%), VALU
+            # issue (%), and the fp16 MFMA flops the two kernels execute per launch
+            "mfma_util_pct": ctr.get("mfma_util_pct"), "valu_busy_pct": ctr.get("valu_busy_pct"),
+            "mfma_flops_executed_per_launch": ctr.get("mfma_flops_executed_per_launch")}
 
     def stage_report(r, out_bytes):
         return {
