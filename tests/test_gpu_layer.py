@@ -3,7 +3,9 @@ workload: the tiny fp32 layer, the production-width T=512 layer, the 36-layer
 T=2048 stack (sampled: the launch the benchmark times, checked on chosen
 layers and value heads), the continuation sweep, and the long varlen batch.
 
-Also: bitwise determinism, and split invariance of the path ("Round 30
+Also: bitwise determinism, a long sequence alone equal to the same sequence
+packed with another, graph replays of the layer equal to the eager call, and
+split invariance of the path ("Round 30
 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 2: the
 token-blocked scan must equal the single pass) -- bitwise for splits on the
 16-token chunk grid, within tolerance for any other split.
@@ -179,3 +181,64 @@ def test_stages_equal_layer_entry_point(gpu):
     assert np.array_equal(np_(st.y).view(np.uint16), np_(ly.y).view(np.uint16))
     assert np.array_equal(np_(st.state), np_(ly.state))
     assert np.array_equal(np_(st.hist), np_(ly.hist))
+
+
+def _single_vs_packed(w1, w2):
+    # one long sequence alone == the same sequence packed first with a short
+    # second one, bitwise: y of its rows, its state and its history
+    inp2 = synth.layer_inputs(w2)
+    T1 = w1.seqlens[0]
+    inp1 = dict(inp2, hist=inp2["hist"][:1], S0=inp2["S0"][:1])
+    for k in ("qkv", "a", "b", "z"):
+        inp1[k] = inp2[k][:T1]
+    banner("gdn_prefill_layer", "single", w1.name, f"T={T1}", w1.io)
+    one = _run_layer(w1, inp1)
+    banner("gdn_prefill_layer", "packed", w2.name, f"lens={w2.seqlens}", w2.io)
+    packed = _run_layer(w2, inp2)
+    assert np.array_equal(np_(one.y).view(np.uint8), np_(packed.y)[:T1].view(np.uint8))
+    assert np.array_equal(np_(one.state)[0].view(np.uint32), np_(packed.state)[0].view(np.uint32))
+    assert np.array_equal(np_(one.hist)[0].view(np.uint8), np_(packed.hist)[0].view(np.uint8))
+    return inp1, one
+
+
+@pytest.mark.parametrize("io", ["f16", "f32"])
+def test_long_sequence_alone_equals_packed(gpu, io):
+    hk, hv = (16, 48) if io == "f16" else (2, 6)
+    kw = dict(hk=hk, hv=hv, io=io, out=io, seed=(31,), s0_std=0.05, hist_std=1.0)
+    w1 = synth.Workload(f"long_{io}", seqlens=(1500,), **kw)
+    w2 = synth.Workload(f"long_plus_short_{io}", seqlens=(1500, 5), **kw)
+    inp1, one = _single_vs_packed(w1, w2)
+    if io == "f32":
+        ref = orc.layer(orc.Dims(hk, hv), w1.cu_seqlens(), inp1)
+        _check_layer(w1, one, ref, io)
+
+
+def test_layer_graph_replay_matches_eager(gpu):
+    # gdn_prefill_layer captured in a graph: every replay, with eager work and
+    # synchronisation between replays, equals the eager call bitwise
+    w = synth.Workload("long_graph", hk=16, hv=48, seqlens=(1200,), seed=(33,), s0_std=0.05,
+                       hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", "graph replay", w.name)
+    eager = _run_layer(w, inp)
+    buf = LayerBuffers.create(w, inp)
+    ws = buf.workspace()
+    hist0, state0 = buf.hist.clone(), buf.state.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        buf.run_layer(ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        buf.run_layer(ws)
+    for r in range(3):
+        buf.hist.copy_(hist0)
+        buf.state.copy_(state0)
+        buf.y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(buf.y).view(np.uint16), np_(eager.y).view(np.uint16)), r
+        assert np.array_equal(np_(buf.state).view(np.uint32), np_(eager.state).view(np.uint32)), r
+        assert np.array_equal(np_(buf.hist).view(np.uint16), np_(eager.hist).view(np.uint16)), r
