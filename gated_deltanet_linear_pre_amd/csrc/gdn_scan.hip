@@ -828,19 +828,19 @@ static int64_t scan_slots(const gdn_shape &s)
 
 // ---- the layer's pre stage fused into the prep step ------------------------
 //
-// One block per (chunk, key head j) computes, for the chunk's 16 tokens, the
-// pre stage of exactly the channels the prep step needs: q and k of key head
-// j (conv, SiLU, L2 norm) straight into LDS and the group's gates, and
-// without RAW_V also v of the group's value heads (conv, SiLU) to the vc
-// buffer the chunk kernel reads (with RAW_V the chunk kernel forms v from the
-// raw rows and carries those channels' history); then it builds the slots
-// like scan_prep_kernel.  The normalised q and k and the gates never go
+// With fp32 io, one block per (chunk, key head j) computes, for the chunk's
+// 16 tokens, the pre stage of exactly the channels the prep step needs: q and
+// k of key head j (conv, SiLU, L2 norm) straight into LDS, the group's gates,
+// and v of the group's value heads (conv, SiLU) to the vc buffer the chunk
+// kernel reads; then it builds the slots like scan_prep_kernel.  (With fp16
+// io, layer_prep_pair_kernel below does the same for q, k and the gates of two
+// chunks per block, and the chunk kernel forms v from the raw rows.)  The normalised q and k and the gates never go
 // through memory.  The arithmetic is that of gdn_pre (the same per-element
 // expressions), so the layer's results equal the staged path's bit for bit.
 // History carry without a race: only the chunk-0 blocks read the old history,
 // each for its own channels, and the same block writes the new history of
 // those channels after a barrier.
-template <typename TI, bool RAW_V>
+template <typename TI>
 __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDims d)
 {
     __shared__ __attribute__((aligned(16))) PrepShared sm;
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
     // weight loads and the rows of X its tokens read, all unconditional (rows
     // past the chunk's end repeat its last row), waits for them once, and then
     // walks its tokens with no load behind a store.
-    const int units = RAW_V ? 2 : 2 + G;  // RAW_V: v is the chunk kernel's
+    const int units = 2 + G;
     const int P = units > 8 ? 2 : CT / units;
     auto unit_base = [&](int u) {
         return u == 0 ? j * 128 : u == 1 ? (hk + j) * 128 : (2 * hk + j * G + (u - 2)) * 128;
@@ -971,6 +971,140 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
     prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c), nv, g_next, b_next, load_gb);
 }
 
+// The fp16 layer path's prep step: what layer_prep_kernel does for one chunk,
+// without v (the chunk kernel forms it), for two consecutive chunks per block.  Each 16-lane row
+// has one task per chunk, q or k of key head j for two of its tokens; both
+// chunks' rows are requested up front, so those of the second are in flight
+// while the block builds the first chunk's slots, and with half as many
+// blocks all of them are resident at once.  Same per-element arithmetic as
+// gdn_pre, so the results equal the staged path's bit for bit.
+__global__ __launch_bounds__(256) void layer_prep_pair_kernel(LayerPrepArgs p, PrepDims d)
+{
+    __shared__ __attribute__((aligned(16))) PrepShared sm;
+    __shared__ float sGate[2][LAYER_G_MAX][2][CT];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15;
+    const int per_seq = (d.n_chunk_max + 1) >> 1;
+    const int n = blockIdx.x / per_seq;
+    const int c0 = 2 * (int)(blockIdx.x - n * per_seq);
+    const int j = blockIdx.y;
+    const int cu0 = p.cu[n];
+    const int T_n = p.cu[n + 1] - cu0;
+    if (c0 * CT >= T_n) return;
+    const bool two = (c0 + 1) * CT < T_n;  // uniform per block
+    const int nv0 = min(CT, T_n - c0 * CT);
+    const int nv1 = two ? min(CT, T_n - (c0 + 1) * CT) : 0;
+    const int hk = d.hk, hv = d.hv, G = d.G, C = d.C;
+    const _Float16 *qkv = static_cast<const _Float16 *>(p.qkv);
+    const _Float16 *cw = static_cast<const _Float16 *>(p.conv_w);
+    _Float16 *hist = static_cast<_Float16 *>(p.hist) + (int64_t)n * 3 * C;
+    const f4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+    // task of this row: unit u (0: q, 1: k of key head j), tokens t0, t0 + 1
+    // of each chunk; lane l16 takes channels 4 l16 .. + 3 and 64 + 4 l16 .. + 3
+    const int task = wave * 4 + (lane >> 4);
+    const int u = task >> 3, t0 = 2 * (task & 7);
+    const int ch = (u == 0 ? j : hk + j) * 128 + l16 * 4;
+    // row xi of X = [history (3 rows); the sequence's tokens], channel c
+    auto xrow = [&](int64_t xi, int c) { return xi < 3 ? hist + xi * C + c : qkv + (cu0 + xi - 3) * C + c; };
+    // weights (fp16, element (4 m + tap) of the lane's channel m = 0..7), then
+    // the five X rows of the task's two tokens in each chunk; rows past a
+    // chunk's end repeat its last row (valid memory, results unused)
+    Raw8<_Float16> wr[4], xa[5], xb[5];
+    auto load_w = [&]() {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wr[k].load(cw + (int64_t)(ch + 64 * (k >> 1)) * 4 + (k & 1) * 8);
+    };
+    load_w();
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+        xa[i].load_split(xrow(min((int64_t)c0 * CT + t0 + i, (int64_t)c0 * CT + nv0 + 2), ch));
+    if (two) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+            xb[i].load_split(xrow(min((int64_t)(c0 + 1) * CT + t0 + i, (int64_t)(c0 + 1) * CT + nv1 + 2), ch));
+    }
+    // conv, SiLU and the L2 norm of the task's tokens of one chunk, into sQ / sK
+    auto conv = [&](const Raw8<_Float16> (&x)[5], int nv) {
+        const int nt = max(0, min(2, nv - t0));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = t0 + i;
+            float sv[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float acc = conv4(wr[e >> 1].get((e & 1) * 4 + 0), wr[e >> 1].get((e & 1) * 4 + 1),
+                                        wr[e >> 1].get((e & 1) * 4 + 2), wr[e >> 1].get((e & 1) * 4 + 3),
+                                        x[i].get(e), x[i + 1].get(e), x[i + 2].get(e), x[i + 3].get(e));
+                sv[e] = silu_fast(acc);
+                ss = fmaf(sv[e], sv[e], ss);
+            }
+            ss = row_sum16(ss);
+            const float sc = rsqrt_fast(ss + d.eps_l2);
+            float *dst = u == 0 ? &sm.sQ[t][l16 * 4] : &sm.sK[t][l16 * 4];
+            *reinterpret_cast<f4 *>(dst) = i < nt ? f4{sv[0] * sc, sv[1] * sc, sv[2] * sc, sv[3] * sc} : z4;
+            *reinterpret_cast<f4 *>(dst + 64) = i < nt ? f4{sv[4] * sc, sv[5] * sc, sv[6] * sc, sv[7] * sc} : z4;
+        }
+    };
+    conv(xa, nv0);
+
+    // gates of the group's value heads for both chunks, token t of head gh of
+    // chunk k at sGate[k][gh][.][t] (zero past the end)
+    if (wave == CHUNK_PREP_THREADS / 64 - 1) {
+        for (int i = lane; i < 2 * G * CT; i += 64) {
+            const int k = i / (G * CT), r = i - k * G * CT;
+            const int gh = r / CT, t = r - gh * CT, h = j * G + gh;
+            float g = 0.f, bt = 0.f;
+            if (t < (k == 0 ? nv0 : nv1)) {
+                const int64_t e = ((int64_t)cu0 + (c0 + k) * CT + t) * hv + h;
+                gates(ld1(static_cast<const _Float16 *>(p.a) + e), ld1(static_cast<const _Float16 *>(p.dt_bias) + h),
+                      ld1(static_cast<const _Float16 *>(p.A_log) + h), ld1(static_cast<const _Float16 *>(p.b) + e),
+                      g, bt);
+            }
+            sGate[k][gh][0][t] = g;
+            sGate[k][gh][1][t] = bt;
+        }
+    }
+    __syncthreads();
+
+    // the new history of q and k of key head j (the block of chunk 0): X rows
+    // T_n .. T_n + 2; for T_n + r < 3 that is old history row T_n + r > r,
+    // not yet overwritten: all three are read before the first write
+    if (c0 == 0 && tid < 32) {
+        const int hc = ((tid >> 4) == 0 ? j : hk + j) * 128 + l16 * 4;
+        Raw8<_Float16> v[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) v[r].load_split(xrow((int64_t)T_n + r, hc));
+        wait_vmem_all();
+#pragma unroll
+        for (int r = 0; r < 3; ++r) v[r].store_split(hist + (int64_t)r * C + hc);
+    }
+
+    float g_next = 0.f, b_next = 0.f;
+    auto load_gb0 = [&](int gh, float &gl, float &bl) {
+        gl = sGate[0][gh][0][l16];
+        bl = sGate[0][gh][1][l16];
+    };
+    if (wave < G) load_gb0(wave, g_next, b_next);
+    prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c0), nv0, g_next, b_next, load_gb0);
+    if (!two) return;
+
+    load_w();  // (again: not held across the first chunk's slots)
+    __syncthreads();  // every wave is done with the first chunk's LDS
+    conv(xb, nv1);
+    __syncthreads();
+    auto load_gb1 = [&](int gh, float &gl, float &bl) {
+        gl = sGate[1][gh][0][l16];
+        bl = sGate[1][gh][1][l16];
+    };
+    g_next = 0.f;
+    b_next = 0.f;
+    if (wave < G) load_gb1(wave, g_next, b_next);
+    prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c0 + 1), nv1, g_next, b_next, load_gb1);
+}
+
 static PrepDims prep_dims(const gdn_shape &s)
 {
     PrepDims pd;
@@ -1021,13 +1155,14 @@ hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const 
     const dim3 grid((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk);
     if (s.io_dtype == GDN_F16) {
         // v of the value heads is formed in the chunk kernel (VRawArgs)
-        hipLaunchKernelGGL((layer_prep_kernel<_Float16, true>), grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+        const dim3 pgrid((unsigned)(s.n_seq * (int64_t)((pd.n_chunk_max + 1) / 2)), s.hk);
+        hipLaunchKernelGGL(layer_prep_pair_kernel, pgrid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const VRawArgs vr{lp.qkv, lp.conv_w, lp.hist, pd.C};
         return launch_chunk(s, a, st, &vr);
     }
-    hipLaunchKernelGGL((layer_prep_kernel<float, false>), grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+    hipLaunchKernelGGL(layer_prep_kernel<float>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_chunk(s, a, st);
