@@ -4,8 +4,8 @@ T=2048 stack (sampled: the launch the benchmark times, checked on chosen
 layers and value heads), the continuation sweep, and the long varlen batch.
 
 Also: bitwise determinism, a long sequence alone equal to the same sequence
-packed with another, graph replays of the layer equal to the eager call, and
-split invariance of the path ("Round 30
+packed with another, graph replays of the layer equal to the eager call, key
+heads shared by 8 and 10 value heads, and split invariance of the path ("Round 30
 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 2: the
 token-blocked scan must equal the single pass) -- bitwise for splits on the
 16-token chunk grid, within tolerance for any other split.
@@ -242,3 +242,25 @@ def test_layer_graph_replay_matches_eager(gpu):
         assert np.array_equal(np_(buf.y).view(np.uint16), np_(eager.y).view(np.uint16)), r
         assert np.array_equal(np_(buf.state).view(np.uint32), np_(eager.state).view(np.uint32)), r
         assert np.array_equal(np_(buf.hist).view(np.uint16), np_(eager.hist).view(np.uint16)), r
+
+
+@pytest.mark.parametrize("hv", [8, 10], ids=["group8_fused", "group10_staged"])
+def test_layer_group_sizes_match_oracle_and_stages(gpu, hv):
+    # one key head shared by 8 value heads (the largest group the fused prep
+    # takes) and by 10 (the layer then runs the three stages): against the
+    # oracle, and bit for bit against gdn_pre + gdn_scan + gdn_post
+    lens = (70, 0, 33)
+    w = synth.Workload(f"group{hv}", hk=1, hv=hv, seqlens=lens, seed=(35,), s0_std=0.05, hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", w.name, f"lens={lens}")
+    ly = _run_layer(w, inp)
+    ref = orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp)
+    _check_layer(w, ly, ref, w.out)
+    st = LayerBuffers.create(w, inp)
+    st.run_pre()
+    st.run_scan()
+    st.run_post()
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(st.y).view(np.uint16), np_(ly.y).view(np.uint16))
+    assert np.array_equal(np_(st.state).view(np.uint32), np_(ly.state).view(np.uint32))
+    assert np.array_equal(np_(st.hist).view(np.uint16), np_(ly.hist).view(np.uint16))
