@@ -971,13 +971,14 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
     prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c), nv, g_next, b_next, load_gb);
 }
 
-// The fp16 layer path's prep step: what layer_prep_kernel does for one chunk,
-// without v (the chunk kernel forms it), for two consecutive chunks per block.  Each 16-lane row
-// has one task per chunk, q or k of key head j for two of its tokens; both
-// chunks' rows are requested up front, so those of the second are in flight
-// while the block builds the first chunk's slots, and with half as many
-// blocks all of them are resident at once.  Same per-element arithmetic as
-// gdn_pre, so the results equal the staged path's bit for bit.
+// The fp16 layer path's prep step: what layer_prep_kernel does for one
+// chunk, without v (the chunk kernel forms it), for two consecutive chunks
+// per block.  Each 16-lane row has one task per chunk, q or k of key head j
+// for two of its tokens; both chunks' rows are requested up front, so those
+// of the second are in flight while the block builds the first chunk's slots,
+// and with half as many blocks all of them are resident at once.  Same
+// per-element arithmetic as gdn_pre, so the results equal the staged path's
+// bit for bit.
 __global__ __launch_bounds__(256) void layer_prep_pair_kernel(LayerPrepArgs p, PrepDims d)
 {
     __shared__ __attribute__((aligned(16))) PrepShared sm;
