@@ -14,8 +14,10 @@ Prints ONE JSON line: tokens/s of the layer path with fp16 output (the
 headline) and fp32 output; the staged path (gdn_pre, gdn_scan, gdn_post) with
 per-stage times from HIP events recorded on the launch stream inside the
 timed region; the scan's roofline fraction (gdn_scan of the staged path);
-gdn_step decode timings; and the fp64 oracle timed on the host cores on a
-bounded sample.
+gdn_step decode timings; the long varlen batch (36 layers of four packed
+sequences, T = 16384, 8192, 2048 and 511, fp32 output) through
+gdn_prefill_layer; and the fp64 oracle timed on the host cores on a bounded
+sample of both workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -78,11 +80,22 @@ def load_counters():
     return d
 
 
-def cpu_baseline(budget_s=15.0, layers_total=36):
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(budget_s=12.0, layers_total=36):
     """The fp64 oracle, as it stands, on whole layers of the same workload
     (T=2048, all 48 value heads, pre+scan+post), one layer after another until
     ~budget_s of oracle time; tokens/s is scaled to the 36-layer pass the
-    metric counts (T / (mean seconds per layer x 36))."""
+    metric counts (T / (mean seconds per layer x 36)).  Also one layer on one
+    thread."""
     import numpy as np
     from gated_deltanet_linear_pre_amd import synth
     from oracle import gdn_oracle as orc
@@ -96,11 +109,41 @@ def cpu_baseline(budget_s=15.0, layers_total=36):
         orc.layer(dims, w.cu_seqlens(), inp)
         times.append(time.perf_counter() - t0)
     per_layer = float(np.mean(times))
+    cores = orc.max_threads()
+    inp = synth.layer_inputs(w, 0)
+    orc.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        orc.layer(dims, w.cu_seqlens(), inp)
+        one = time.perf_counter() - t0
+    finally:
+        orc.set_threads(cores)
     return dict(value=round(w.total_T / (per_layer * layers_total), 2), unit="tokens/s",
-                cores=orc.max_threads(), kind="oracle",
+                cores=cores, kind="oracle",
                 sample=f"{len(times)} of the 36 layers (layers 0..{len(times) - 1}), each full "
                        f"T=2048, all 48 value heads, pre+scan+post in fp64; "
-                       f"{per_layer:.2f} s per layer, scaled to 36 layers")
+                       f"{per_layer:.2f} s per layer, scaled to 36 layers",
+                cpu_model=cpu_model(),
+                one_core={"s_per_layer": round(one, 3), "tokens_per_s": round(w.total_T / (one * 36), 2),
+                          "sample": "layer 0, T=2048, all 48 value heads, 1 thread, scaled to 36 layers"})
+
+
+def cpu_baseline_varlen(layers_total=36):
+    """The fp64 oracle on one whole layer of the long varlen batch (layer 0:
+    all four sequences, all 48 value heads), extrapolated to 36 layers."""
+    from gated_deltanet_linear_pre_amd import synth
+    from oracle import gdn_oracle as orc
+
+    w = synth.WORKLOADS["prod36_varlen4_fp32out"]
+    inp = synth.layer_inputs(w, 0)
+    t0 = time.perf_counter()
+    orc.layer(orc.Dims(w.hk, w.hv), w.cu_seqlens(), inp)
+    sec = time.perf_counter() - t0
+    return dict(value=round(w.total_T / (sec * layers_total), 2), unit="tokens/s",
+                cores=orc.max_threads(), kind="oracle",
+                sample=f"layer 0 of 36 ({w.total_T} tokens, all 48 value heads, pre+scan+post "
+                       f"in fp64), {sec:.2f} s; tokens/s extrapolated to 36 layers as "
+                       f"T / (36 x that time)")
 
 
 def main():
@@ -117,7 +160,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by value heads with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path would shard by value heads, with no exchange inside it)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -325,6 +368,76 @@ def main():
                 "bytes_per_layer": byts, "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "hbm_frac_graph": round(byts / (us_g * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    def varlen(steps, warmup):
+        # the long varlen batch through gdn_prefill_layer, 36 layers in order,
+        # each with its own inputs (drawn on the device), state, history and
+        # output; then gdn_scan alone over 36 per-layer states (the roofline
+        # kernel), reading one layer's intermediates
+        wv = synth.WORKLOADS["prod36_varlen4_fp32out"]
+        Tv = wv.total_T
+        lv = [synth.layer_inputs_device(wv, l, dev) for l in range(L)]
+        cuv = upload(wv.cu_seqlens(), dev)
+        shape = B.make_shape(hk, hv, wv.n_seq, Tv, wv.max_T, io="f16", out="f32")
+        ys = [torch.empty((Tv, hv * 128), dtype=torch.float32, device=dev) for _ in range(L)]
+        ws = scratch(B.gdn_prefill_workspace_bytes(shape), dev)
+
+        def step():
+            for l, d in enumerate(lv):
+                B.gdn_prefill_layer(shape, cuv, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"],
+                                    d["dt_bias"], d["z"], d["gamma"], d["hist"], d["S0"], ys[l], ws,
+                                    stream=stream)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        del ys, ws
+        # gdn_scan alone: one layer's intermediates from gdn_pre, 36 states
+        f = dict(dtype=torch.float32, device=dev)
+        iq, ik = torch.empty((Tv, hk, 128), **f), torch.empty((Tv, hk, 128), **f)
+        iv, io_ = torch.empty((Tv, hv, 128), **f), torch.empty((Tv, hv, 128), **f)
+        ig, ib = torch.empty((Tv, hv), **f), torch.empty((Tv, hv), **f)
+        d0 = lv[0]
+        B.gdn_pre(shape, cuv, d0["qkv"], d0["conv_w"], d0["a"], d0["b"], d0["A_log"], d0["dt_bias"],
+                  d0["hist"].clone(), iq, ik, iv, ig, ib, stream=stream)
+        sws = scratch(B.gdn_scan_workspace_bytes(shape), dev)
+        states = [d["S0"] for d in lv]
+
+        def scans():
+            for S in states:
+                B.gdn_scan(shape, cuv, iq, ik, iv, ig, ib, S, io_, sws, stream=stream)
+        scans()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            scans()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        scan_us = e0.elapsed_time(e1) * 1e3 / (steps * L)
+        del lv, iq, ik, iv, io_, ig, ib, sws
+        torch.cuda.empty_cache()
+        tf = scan_flops(Tv, hv) / (scan_us * 1e-6) / 1e12
+        return {"workload": wv.name, "layers": L, "seqlens": list(wv.seqlens), "T_total": Tv,
+                "io": "fp16", "state": "fp32", "out": "fp32",
+                "value": round(Tv / (ms / 1e3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 3),
+                "inputs": "drawn on the device (torch Philox), same shapes and distributions as the "
+                          "parity tests' host-drawn inputs",
+                "roofline": {"bound": "mfma", "kernel": "gdn_scan (scan_prep_kernel + scan_chunk_kernel)",
+                             "achieved": round(tf, 3), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "us_per_call": round(scan_us, 1),
+                             "flops_per_launch": scan_flops(Tv, hv)},
+                "critical_path_chunk_steps": (max(wv.seqlens) + 15) // 16,
+                "cpu_baseline": None}
+
+    log("timing the long varlen batch (36 layers, T = 16384 + 8192 + 2048 + 511)")
+    var = varlen(max(3, args.steps // 4), 1)
+
     log("timing gdn_step decode")
     dec = [decode(b) for b in (1, 8, 64)]
 
@@ -339,7 +452,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 (state, elementwise); contractions as split fp16 x3 on MFMA",
         "data": "synthetic",
         "config": {"workload": w16.name, "layers": L, "T": T, "batch": 1, "hk": hk, "hv": hv,
                    "head_dim": 128, "io": "fp16", "state": "fp32", "out": "fp16",
@@ -351,12 +464,15 @@ def main():
                             "ms_per_step": round(r16["ms_per_step"], 4), **stage_report(r16, 2)},
         "staged_fp32_out": {"value": round(T / (r32["ms_per_step"] / 1e3), 1),
                             "ms_per_step": round(r32["ms_per_step"], 4), **stage_report(r32, 4)},
+        "varlen4": var,
         "decode_gdn_step": dec,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host cores")
         res["cpu_baseline"] = cpu_baseline()
+        log("timing the fp64 oracle on one layer of the long varlen batch")
+        res["varlen4"]["cpu_baseline"] = cpu_baseline_varlen()
     print(json.dumps(res), flush=True)
 
 

@@ -20,7 +20,9 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
-int check_shape(const gdn_shape *s)
+} // namespace
+
+int gdn::check_shape(const gdn_shape *s)
 {
     if (!s) return GDN_E_NULL;
     if (s->io_dtype != GDN_F32 && s->io_dtype != GDN_F16) return GDN_E_DTYPE;
@@ -41,6 +43,10 @@ int check_shape(const gdn_shape *s)
     if ((int64_t)s->n_seq * s->hv * 4 >= ((int64_t)1 << 31)) return GDN_E_SHAPE;
     return GDN_OK;
 }
+
+namespace {
+
+using gdn::check_shape;
 
 #define REQ(p)                                  \
     do {                                        \
@@ -80,22 +86,55 @@ int check_post(const float *o, const void *z, const void *gamma, const void *y)
     return GDN_OK;
 }
 
+} // namespace
+
+// The caller's buffers of gdn_prefill_layer (everything but the workspace).
+int gdn::check_layer_args(const int32_t *cu, const void *qkv, const void *conv_w, const void *a,
+                          const void *b, const void *A_log, const void *dt_bias, const void *z,
+                          const void *gamma, const void *hist, const float *state, const void *y)
+{
+    REQ(cu); REQ(qkv); REQ(conv_w); REQ(a); REQ(b); REQ(A_log); REQ(dt_bias); REQ(z); REQ(gamma);
+    REQ(hist); REQ(state); REQ(y);
+    ALN(cu, 4); ALN(a, 4); ALN(b, 4); ALN(A_log, 4); ALN(dt_bias, 4);
+    ALN(qkv, 16); ALN(conv_w, 16); ALN(hist, 16); ALN(state, 16); ALN(z, 16); ALN(gamma, 16);
+    ALN(y, 16);
+    return GDN_OK;
+}
+
+namespace {
+
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
     size_t qn, kn, vc, g, beta, o, scan, total;
 };
 
+// Which path gdn_prefill_layer takes for a shape: the pre stage fused into the
+// scan's prep step when a key head has at most LAYER_G_MAX value heads (with
+// fp16 inputs v is formed inside the chunk kernel too), else the three stages.
+enum class LayerPath { fused_f16, fused_f32, staged };
+
+LayerPath layer_path(const gdn_shape *s)
+{
+    if (s->hv / s->hk > gdn::LAYER_G_MAX) return LayerPath::staged;
+    return s->io_dtype == GDN_F16 ? LayerPath::fused_f16 : LayerPath::fused_f32;
+}
+
+// The layer workspace holds what the path writes and reads back: o and the
+// scan scratch always; the fp32 v when the fused prep forms it (fp32 inputs);
+// q, k, v and the gates only on the staged path.
 Carve carve(const gdn_shape *s)
 {
     const size_t T = (size_t)s->total_T;
+    const LayerPath path = layer_path(s);
+    const bool staged = path == LayerPath::staged;
     Carve c;
     size_t off = 0;
-    c.qn = off; off += round256(T * s->hk * 128 * sizeof(float));
-    c.kn = off; off += round256(T * s->hk * 128 * sizeof(float));
-    c.vc = off; off += round256(T * s->hv * 128 * sizeof(float));
-    c.g = off; off += round256(T * s->hv * sizeof(float));
-    c.beta = off; off += round256(T * s->hv * sizeof(float));
+    c.qn = off; off += staged ? round256(T * s->hk * 128 * sizeof(float)) : 0;
+    c.kn = off; off += staged ? round256(T * s->hk * 128 * sizeof(float)) : 0;
+    c.vc = off; off += path != LayerPath::fused_f16 ? round256(T * s->hv * 128 * sizeof(float)) : 0;
+    c.g = off; off += staged ? round256(T * s->hv * sizeof(float)) : 0;
+    c.beta = off; off += staged ? round256(T * s->hv * sizeof(float)) : 0;
     c.o = off; off += round256(T * s->hv * 128 * sizeof(float));
     c.scan = off; off += round256(gdn::scan_workspace_bytes(*s));
     c.total = off;
@@ -185,6 +224,8 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     int st = check_shape(shape);
     if (st) return st;
     if (shape->total_T == 0) return GDN_OK;
+    st = gdn::check_layer_args(cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist, state, y);
+    if (st) return st;
     REQ(workspace);
     ALN(workspace, 256);
     const Carve c = carve(shape);
@@ -197,6 +238,8 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     float *beta = reinterpret_cast<float *>(ws + c.beta);
     float *o = reinterpret_cast<float *>(ws + c.o);
     float *sws = reinterpret_cast<float *>(ws + c.scan);
+    // (on the fused paths the unused intermediates have no room of their own:
+    // their pointers alias the next region and are never dereferenced)
     st = check_pre(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta);
     if (st) return st;
     st = check_scan(cu_seqlens, qn, kn, vc, g, beta, state, o, sws);
@@ -205,7 +248,7 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o, sws};
-    if (shape->hv / shape->hk <= gdn::LAYER_G_MAX) {
+    if (layer_path(shape) != LayerPath::staged) {
         // pre fused into the scan's prep step: q, k and the gates stay on chip
         const gdn::LayerPrepArgs lp{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, vc, sws};
         if (gdn::launch_layer_scan(*shape, lp, sa, s) != hipSuccess) return GDN_E_LAUNCH;

@@ -63,6 +63,14 @@ struct StepArgs {
     void *y;
 };
 
+// The shape checks every entry point runs first (GDN_OK or a gdn_status).
+int check_shape(const gdn_shape *s);
+// Null and alignment checks of gdn_prefill_layer's buffers other than the
+// workspace (GDN_OK or a gdn_status).
+int check_layer_args(const int32_t *cu, const void *qkv, const void *conv_w, const void *a,
+                     const void *b, const void *A_log, const void *dt_bias, const void *z,
+                     const void *gamma, const void *hist, const float *state, const void *y);
+
 hipError_t launch_pre(const gdn_shape &s, const PreArgs &a, hipStream_t st);
 hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st);
 hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const ScanArgs &a,

@@ -26,11 +26,12 @@
 // accumulation, each fp32 operand x split into hi = fp16(x) and
 // lo = fp16(x - hi): x*y ~ hi_x hi_y + hi_x lo_y + lo_x hi_y, good to about
 // 2^-21 relative per product (the dropped lo_x lo_y term and the rounding of
-// lo).  k, q and the state are scaled by 16 (exactly) so that the lo parts
-// stay out of fp16 subnormals; the state stays fp32 in the MFMA accumulators.
-// Operands must stay inside the fp16 range after scaling (|state| < 4e3,
-// |v|, |u| < 6.5e4); beyond it the result turns to inf/NaN, never silently
-// wrong.
+// lo).  k, q and the state are scaled by 16 (exactly); the state stays fp32
+// in the MFMA accumulators.  The low halves of the operands whose scale
+// follows the data (state, B, U w, U) are carried x 2^10 in products of their
+// own (see LO_SCALE), so the split stays accurate for small values too.
+// Range: |16 state|, |B|, |U w| and |U| below 65504; past it a scaled low half
+// overflows and the results turn to inf/NaN.
 //
 // gfx950 mapping.
 // * gdn_scan_prep (parallel over sequence x chunk x key head):
@@ -65,9 +66,11 @@
 //   of the block's channels from the raw qkv rows the copy wave brings (conv
 //   with the history, SiLU: the pre stage's expressions) and carries their
 //   history, so the fp32 v never goes through memory.
-// * Block order is XCD-aware: blocks are dealt round-robin to the 8 XCDs, so
-//   the index is permuted to give each XCD whole key-head groups, whose
-//   key-head slots are then shared in one L2.
+// * Block order: longest sequence first (its chain of chunk steps is the
+//   critical path of a packed batch), and XCD-aware: blocks are dealt
+//   round-robin to the 8 XCDs, so inside each sequence's range the index is
+//   permuted to give each XCD whole key-head groups, whose key-head slots are
+//   then shared in one L2.
 //
 // Determinism: fixed-order MFMA chains, no atomics.  Splitting a sequence at a
 // multiple of 16 tokens gives bit-identical results; other split points agree
@@ -148,6 +151,46 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1, fl
     const h2 r = {(_Float16)__builtin_fmaf((float)h[0], m1, x0),
                   (_Float16)__builtin_fmaf((float)h[1], m1, x1)};
     return __builtin_bit_cast(uint32_t, r);
+}
+// For operands whose scale follows the data (the state, B = beta (v - Lam P),
+// U w, U) the low half is carried multiplied by LO_SCALE = 2^10 and enters
+// its own product, which is scaled back (exactly) by 2^-10 when it is added:
+// lo stays a normal fp16 number down to |x| ~ 2^-13 instead of 2^-3, so the
+// split keeps ~22 bits over 29 binades of magnitude, and past the top of the
+// fp16 range (|x| > 65504 + 2^6) the scaled low half overflows to inf, which
+// the results show.  ms = -LO_SCALE at run time (see lo_pair).
+constexpr float LO_SCALE = 1024.f;
+constexpr float LO_UNSCALE = 1.f / 1024.f;
+__device__ __forceinline__ uint32_t lo_pair_s(uint32_t hi2, float x0, float x1, float ms)
+{
+    const h2 h = __builtin_bit_cast(h2, hi2);
+    const h2 r = {(_Float16)__builtin_fmaf((float)h[0], ms, x0 * LO_SCALE),
+                  (_Float16)__builtin_fmaf((float)h[1], ms, x1 * LO_SCALE)};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ void split4s(const f4 x, h4 &hi, h4 &lo, float ms)
+{
+    u2 h, l;
+    h[0] = hi_pair(x[0], x[1]);
+    h[1] = hi_pair(x[2], x[3]);
+    l[0] = lo_pair_s(h[0], x[0], x[1], ms);
+    l[1] = lo_pair_s(h[1], x[2], x[3], ms);
+    hi = __builtin_bit_cast(h4, h);
+    lo = __builtin_bit_cast(h4, l);
+}
+__device__ __forceinline__ void split8s(const f4 a, const f4 b, h8 &hi, h8 &lo, float ms)
+{
+    u4 h, l;
+    h[0] = hi_pair(a[0], a[1]);
+    h[1] = hi_pair(a[2], a[3]);
+    h[2] = hi_pair(b[0], b[1]);
+    h[3] = hi_pair(b[2], b[3]);
+    l[0] = lo_pair_s(h[0], a[0], a[1], ms);
+    l[1] = lo_pair_s(h[1], a[2], a[3], ms);
+    l[2] = lo_pair_s(h[2], b[0], b[1], ms);
+    l[3] = lo_pair_s(h[3], b[2], b[3], ms);
+    hi = __builtin_bit_cast(h8, h);
+    lo = __builtin_bit_cast(h8, l);
 }
 __device__ __forceinline__ void split4(const f4 x, h4 &hi, h4 &lo, float m1)
 {
@@ -436,10 +479,28 @@ __global__ __launch_bounds__(256) void scan_prep_kernel(ScanArgs p, PrepDims d)
 }
 
 struct ChunkDims {
-    int hk, hv, G;
+    int hk, hv, G, n_seq;
     float m1;         // -1 (see lo_pair)
+    float ms;         // -LO_SCALE (see lo_pair_s)
     int64_t vh_base;
 };
+
+// The sequence of rank r when the sequences are sorted by decreasing length
+// (ties by index).  Lane l < n_seq takes sequence l and counts the sequences
+// that come before it; every wave computes the same answer.
+constexpr int SEQ_RANK_MAX = 64;
+__device__ __forceinline__ int seq_of_rank(const int32_t *cu, int n_seq, int r)
+{
+    const int lane = threadIdx.x & 63;
+    const int len = lane < n_seq ? cu[lane + 1] - cu[lane] : -1;
+    int before = 0;
+    for (int m = 0; m < n_seq; ++m) {
+        const int lm = __shfl(len, m);
+        before += (lm > len || (lm == len && m < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(lane < n_seq && before == r);
+    return hit ? __builtin_ctzll(hit) : r;
+}
 
 // A block owns 32 value channels of one (sequence, value head): two row groups
 // of 16 channels, and each row group is shared by a pair of waves, one per half
@@ -501,15 +562,19 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     const int lane = tid & 63, l16 = lane & 15, kk = lane >> 4;
     const f4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-    // XCD-aware work index -> (sequence n, value head h, channel block rb)
+    // block -> (sequence n, value head h, channel block rb): the sequences'
+    // ranges of hv * RB blocks in order of decreasing length, so the longest
+    // recurrence starts first (up to SEQ_RANK_MAX sequences; beyond that in
+    // index order); inside a range (a multiple of 8 blocks when hv is even)
+    // the XCD-aware permutation
     constexpr int RB = 128 / CHUNK_ROWS;
-    const int nb = gridDim.x;
-    int w = (int)blockIdx.x;
-    if ((nb & 7) == 0) w = (w & 7) * (nb >> 3) + (w >> 3);
+    const int per_seq = d.hv * RB;
+    const int rank = (int)blockIdx.x / per_seq;
+    int w = (int)blockIdx.x - rank * per_seq;
+    if ((per_seq & 7) == 0) w = (w & 7) * (per_seq >> 3) + (w >> 3);
     const int rb = w % RB;
-    w /= RB;
-    const int h = w % d.hv;
-    const int n = w / d.hv;
+    const int h = w / RB;
+    const int n = d.n_seq <= SEQ_RANK_MAX ? seq_of_rank(p.cu, d.n_seq, rank) : rank;
     const int j = h / d.G;
     const int hk = d.hk, hv = d.hv;
 
@@ -611,11 +676,10 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
                 const f4 R = sXR[x][2 * g][lane] + sXR[x][2 * g + 1][lane];
                 const f4 U = sU[x][g][lane];
                 h4 uh, ul;
-                split4(U, uh, ul, d.m1);
-                const h4 zh = {};
-                f4 O = mfma_k32(mp, cat(uh, uh), lam * R);
-                O = mfma_k32(cat(lo_half(mp), zh), cat(ul, zh), O);
-                O *= SCALE;
+                split4s(U, uh, ul, d.ms);
+                // (M_hi + M_lo) U_hi, then M_hi U_lo scaled back
+                const f4 O = (mfma_k32(mp, cat(uh, uh), lam * R) +
+                              mfma_k16(lo_half(mp), ul, z4) * LO_UNSCALE) * SCALE;
                 char *ob = reinterpret_cast<char *>(p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + g * 16);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -746,15 +810,15 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         // partial P = K S^T (x256) over this wave's 64 keys
         h8 sh[2], sl[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) split8(S4[2 * i], S4[2 * i + 1], sh[i], sl[i], d.m1);
+        for (int i = 0; i < 2; ++i) split8s(S4[2 * i], S4[2 * i + 1], sh[i], sl[i], d.ms);
         f4 Phh = {0.f, 0.f, 0.f, 0.f}, Phl = Phh, Plh = Phh;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             Phh = mfma_k32(kph[i], sh[i], Phh);
-            Phl = mfma_k32(kph[i], sl[i], Phl);
+            Phl = mfma_k32(kph[i], sl[i], Phl);   // x LO_SCALE
             Plh = mfma_k32(kpl[i], sh[i], Plh);
         }
-        const f4 Pp = (Phh + Phl) + Plh;
+        const f4 Pp = (Phh + Plh) + Phl * LO_UNSCALE;
         sXP[x][wave][lane] = Pp;
         lds_barrier();  // partials visible; every wave is past chunk c - 1
         __builtin_amdgcn_sched_barrier(0);  // nothing below moves up before the barrier
@@ -785,25 +849,24 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) Bm[r] = bet[r] * __builtin_fmaf(-lam[r], P[r], vv[r]);
         h4 bh, bl;
-        split4(Bm, bh, bl, d.m1);
-        // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo
-        const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4);
+        split4s(Bm, bh, bl, d.ms);
+        // U = T B: (T_hi B_hi + T_lo B_hi) + T_hi B_lo (the last scaled back)
+        const f4 U = mfma_k32(tp, cat(bh, bh), z4) + mfma_k16(lo_half(tp), bl, z4) * LO_UNSCALE;
         if (kh == 0) sU[x][grp][lane] = U;
         if (wave == 1) {
             sLam[x][lane] = lam;
             sMp[x][lane] = *reinterpret_cast<const h8 *>(reinterpret_cast<const _Float16 *>(vh + VH_MP) + lane * 8);
         }
         h4 uwh, uwl;
-        split4(U * wu, uwh, uwl, d.m1);
+        split4s(U * wu, uwh, uwl, d.ms);
         const h8 uww = cat(uwh, uwh);
         // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U): this wave's 4 key blocks;
-        // the hi.lo term runs as a zero-padded 16x16x32 chained on the first
-        // product (see mfma_k16)
-        const h4 zh = {};
+        // (K_hi + K_lo)^T (U w)_hi accumulates onto Lam_last S, and the
+        // K_hi^T (U w)_lo product (x LO_SCALE) is scaled back and added
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const f4 C = mfma_k32(kt[i], uww, S4[i] * last);
-            S4[i] = mfma_k32(cat(lo_half(kt[i]), zh), cat(uwl, zh), C);
+            S4[i] = C + mfma_k16(lo_half(kt[i]), uwl, z4) * LO_UNSCALE;
         }
         // partial R = Q S^T (x256) of this chunk from the split of the state
         // before the update; the output wave reads it after the next barrier
@@ -811,10 +874,10 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             Rhh = mfma_k32(qph[i], sh[i], Rhh);
-            Rhl = mfma_k32(qph[i], sl[i], Rhl);
+            Rhl = mfma_k32(qph[i], sl[i], Rhl);   // x LO_SCALE
             Rlh = mfma_k32(qpl[i], sh[i], Rlh);
         }
-        sXR[x][wave][lane] = (Rhh + Rhl) + Rlh;
+        sXR[x][wave][lane] = (Rhh + Rlh) + Rhl * LO_UNSCALE;
     }
     lds_barrier();  // R and U of the last chunk are visible to the output wave
 #pragma unroll
@@ -1127,8 +1190,10 @@ static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_
     cd.hk = s.hk;
     cd.hv = s.hv;
     cd.G = s.hv / s.hk;
+    cd.n_seq = s.n_seq;
     cd.vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
     cd.m1 = -1.f;
+    cd.ms = -LO_SCALE;
     const int64_t blocks = (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS);
     if (vr)
         hipLaunchKernelGGL(scan_chunk_kernel<true>, dim3((unsigned)blocks), dim3(chunk_threads(true)), 0,

@@ -172,3 +172,28 @@ def post_inputs(n_tok: int, hv: int, dv=128, seed=(6,), o_std=8e-4, io="f16") ->
         z=normal(seed, "z", (n_tok, hv * dv), 1.0, dtype=io),
         gamma=normal(seed, "gamma", (dv,), 0.1, mean=1.0, dtype=io),
     )
+
+
+def layer_inputs_device(w: Workload, layer: int, device) -> dict:
+    """One layer's inputs drawn on the device with torch's generator (Philox),
+    with the same shapes, dtypes and distributions as layer_inputs but not the
+    same values: for throughput runs whose inputs are too large to draw on the
+    host in time (the long varlen batch).  Parity checks use layer_inputs."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.default_rng([*map(int, w.layer_seed(layer)), 99]).integers(2**62)))
+    dt = {"f32": torch.float32, "f16": torch.float16}[w.io]
+    T, C, hv, dv, dk, n = w.total_T, w.C, w.hv, w.dv, w.dk, w.n_seq
+
+    def nrm(shape, std, mean=0.0, dtype=dt):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+        return (x + mean).to(dtype)
+
+    A_log = (torch.rand((hv,), generator=g, device=device) * math.log(16.0)).to(dt)
+    return dict(
+        qkv=nrm((T, C), 1.0), conv_w=nrm((C, 4), 0.25), a=nrm((T, hv), 1.0), b=nrm((T, hv), 1.0),
+        A_log=A_log, dt_bias=nrm((hv,), 0.5), z=nrm((T, hv * dv), 1.0), gamma=nrm((dv,), 0.1, 1.0),
+        S0=nrm((n, hv, dv, dk), w.s0_std, dtype=torch.float32) if w.s0_std else
+        torch.zeros((n, hv, dv, dk), device=device, dtype=torch.float32),
+        hist=nrm((n, 3, C), w.hist_std) if w.hist_std else torch.zeros((n, 3, C), device=device, dtype=dt),
+    )

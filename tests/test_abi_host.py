@@ -50,8 +50,16 @@ def test_workspace_bytes():
     per_slot = 16 * 24576 + 48 * 2304   # per 16-token chunk: key-head and value-head parts
     scan = (T // 16 + 1 + 1) * per_slot
     assert B.gdn_scan_workspace_bytes(s) == scan
-    want = 2 * r(T * 16 * 128 * 4) + r(T * 48 * 128 * 4) * 2 + 2 * r(T * 48 * 4) + r(scan)
-    assert B.gdn_prefill_workspace_bytes(s) == want
+    # fused fp16 path (3 value heads per key head): o and the scan scratch only
+    assert B.gdn_prefill_workspace_bytes(s) == r(T * 48 * 128 * 4) + r(scan)
+    # fused fp32 path: the fp32 v as well
+    s32 = shape(total_T=2048, max_T=2048, io="f32")
+    assert B.gdn_prefill_workspace_bytes(s32) == 2 * r(T * 48 * 128 * 4) + r(scan)
+    # staged path (more than 8 value heads per key head): every intermediate
+    st = shape(hk=1, hv=10, total_T=2048, max_T=2048)
+    scan10 = (T // 16 + 2) * (24576 + 10 * 2304)
+    want = 2 * r(T * 128 * 4) + r(T * 10 * 128 * 4) * 2 + 2 * r(T * 10 * 4) + r(scan10)
+    assert B.gdn_prefill_workspace_bytes(st) == want
     assert B.gdn_prefill_workspace_bytes(shape(hv=47)) == 0
     assert B.gdn_scan_workspace_bytes(shape(hv=47)) == 0
     # varlen: at most total_T / 16 + n_seq slots per value head
@@ -193,4 +201,5 @@ def test_step_shape_rules():
 def test_step_null_and_alignment(name):
     assert _step(step_shape(), **{name: None}) == -1
     assert _step(step_shape(), **{name: P + 2}) == -3
+
 
