@@ -19,7 +19,7 @@ GDN_F32, GDN_F16 = 0, 1
 DTYPE_CODE = {"f32": GDN_F32, "f16": GDN_F16}
 
 STATUS = {0: "GDN_OK", -1: "GDN_E_NULL", -2: "GDN_E_SHAPE", -3: "GDN_E_ALIGN",
-          -4: "GDN_E_WORKSPACE", -5: "GDN_E_DTYPE", -6: "GDN_E_LAUNCH"}
+          -4: "GDN_E_WORKSPACE", -5: "GDN_E_DTYPE", -6: "GDN_E_LAUNCH", -7: "GDN_E_TOO_LARGE"}
 
 
 class GdnError(RuntimeError):
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_workspace_bytes.argtypes = [SP]
         L.gdn_prefill_layer.restype = I
         L.gdn_prefill_layer.argtypes = [SP] + [P] * 13 + [S, P]
+        L.gdn_prefill_layer_noalloc.restype = I
+        L.gdn_prefill_layer_noalloc.argtypes = [SP] + [P] * 13
         L.gdn_step.restype = I
         L.gdn_step.argtypes = [SP] + [P] * 12
         _lib = L
@@ -161,6 +163,17 @@ def gdn_prefill_layer(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, z, g
         int(workspace_bytes), _stream(stream))
     if check:
         _check("gdn_prefill_layer", st)
+    return st
+
+
+def gdn_prefill_layer_noalloc(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist,
+                              state, y, stream=None, check=True) -> int:
+    st = lib().gdn_prefill_layer_noalloc(
+        ctypes.byref(shape), *map(_ptr, (cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, z, gamma,
+                                         hist, state, y)),
+        _stream(stream))
+    if check:
+        _check("gdn_prefill_layer_noalloc", st)
     return st
 
 

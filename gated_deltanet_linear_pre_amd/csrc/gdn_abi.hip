@@ -22,6 +22,7 @@ bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
 } // namespace
 
+// (also used by the no-allocation entry point)
 int gdn::check_shape(const gdn_shape *s)
 {
     if (!s) return GDN_E_NULL;
@@ -158,7 +159,8 @@ const char *gdn_status_str(int status)
     case GDN_E_ALIGN: return "a pointer is not aligned as required";
     case GDN_E_WORKSPACE: return "workspace too small";
     case GDN_E_DTYPE: return "unknown dtype";
-    case GDN_E_LAUNCH: return "kernel launch failed";
+    case GDN_E_LAUNCH: return "the HIP runtime rejected a kernel launch or call";
+    case GDN_E_TOO_LARGE: return "the shape needs more workspace than the library's static array holds";
     default: return "unknown status";
     }
 }

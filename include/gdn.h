@@ -24,8 +24,9 @@
  * Pointers are DEVICE pointers on the current HIP device, except `shape`,
  * which is a host pointer read during the call only.  `stream` is a
  * hipStream_t passed as void* (NULL = the default stream).  Every function only
- * enqueues work on `stream`; none synchronises, allocates or keeps state, so
- * calls are re-entrant.  The caller owns every buffer.
+ * enqueues work on `stream`; none synchronises or allocates, and all but
+ * gdn_prefill_layer_noalloc keep no state, so calls are re-entrant.  The
+ * caller owns every buffer.
  *
  * Return value: GDN_OK (0), or a negative gdn_status.  All argument checks
  * run before anything is enqueued, so on error nothing has been launched.
@@ -70,7 +71,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -79,7 +80,8 @@ typedef enum gdn_status {
     GDN_E_ALIGN = -3,     /* a pointer is not aligned as required              */
     GDN_E_WORKSPACE = -4, /* workspace smaller than gdn_prefill_workspace_bytes */
     GDN_E_DTYPE = -5,     /* io_dtype or out_dtype not a gdn_dtype             */
-    GDN_E_LAUNCH = -6     /* the HIP runtime rejected a kernel launch          */
+    GDN_E_LAUNCH = -6,    /* the HIP runtime rejected a kernel launch or call  */
+    GDN_E_TOO_LARGE = -7  /* the shape needs more than GDN_NOALLOC_SCRATCH_BYTES */
 } gdn_status;
 
 typedef enum gdn_dtype {
@@ -223,6 +225,32 @@ int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w,
              const void *a, const void *b, const void *A_log,
              const void *dt_bias, const void *z, const void *gamma, void *hist,
              float *state, void *y, void *stream);
+
+/*
+ * gdn_prefill_layer_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gdn_prefill_layer with the same arguments and results, except
+ * that the workspace is a static device array of GDN_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on every device it runs on until the process
+ * ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); the caller still provides every input and output.
+ *
+ * Shapes whose gdn_prefill_workspace_bytes exceeds GDN_NOALLOC_SCRATCH_BYTES
+ * are rejected with GDN_E_TOO_LARGE before anything is enqueued (at
+ * production width, 16 key and 48 value heads, about 2300 tokens fit).  The
+ * array's device address is looked up on the first call on each device
+ * (GDN_E_LAUNCH if the runtime refuses).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (on different streams,
+ * or from different threads) race and give undefined results; calls in
+ * order on one stream are safe.  Nothing in the array needs to start at
+ * zero: every byte a call reads was written earlier in the same call.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdn_prefill_layer_noalloc(const gdn_shape *shape, const int32_t *cu_seqlens,
+                              const void *qkv, const void *conv_w, const void *a,
+                              const void *b, const void *A_log, const void *dt_bias,
+                              const void *z, const void *gamma, void *hist,
+                              float *state, void *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,14 +26,14 @@ def test_exports_every_declared_symbol(L):
     names = B.declared_symbols()
     assert set(names) == {"gdn_abi_version", "gdn_status_str", "gdn_pre", "gdn_scan",
                           "gdn_scan_workspace_bytes", "gdn_post", "gdn_prefill_workspace_bytes",
-                          "gdn_prefill_layer", "gdn_step"}
+                          "gdn_prefill_layer", "gdn_prefill_layer_noalloc", "gdn_step"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert B.gdn_abi_version() == 3
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    assert B.gdn_abi_version() == 4
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert B.gdn_status_str(code) and B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(-99) == "unknown status"
 
@@ -203,3 +203,22 @@ def test_step_null_and_alignment(name):
     assert _step(step_shape(), **{name: P + 2}) == -3
 
 
+
+def _noalloc(s, **over):
+    args = dict(cu=P, qkv=P, conv_w=P, a=P, b=P, A_log=P, dt_bias=P, z=P, gamma=P, hist=P,
+                state=P, y=P)
+    args.update(over)
+    return B.gdn_prefill_layer_noalloc(s, *args.values(), stream=0, check=False)
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    # every outcome here is decided on the host: no kernel, no runtime call
+    assert _noalloc(shape(hv=47)) == -2
+    assert _noalloc(shape(total_T=0, max_T=0)) == 0
+    assert _noalloc(shape(), y=None) == -1
+    assert _noalloc(shape(), state=P + 4) == -3
+    # more workspace than the library's static array holds
+    big = shape(total_T=100000, max_T=100000)
+    assert B.gdn_prefill_workspace_bytes(big) > 128 << 20
+    assert _noalloc(big) == -7
+    assert B.gdn_status_str(-7) != "unknown status"
