@@ -23,11 +23,11 @@ struct ScanArgs {
     float *ws;  // per-(chunk, value head) prep slots
 };
 
-// Scan workspace: per 16-token chunk, one key-head slot per key head (K, Q
-// and K^T as split fp16 MFMA operands, 24 KB) and one value-head slot per
-// value head (T, M as split fp16 operands plus the chunk's decay vectors).
-constexpr int SCAN_KH_FLOATS = 6144;
-constexpr int SCAN_SLOT_FLOATS = 576;
+// Scan workspace: per 32-token chunk, one key-head slot per key head (K and Q
+// as split fp16 MFMA operands, 32 KB) and one value-head slot per value head
+// (T, M as split fp16 operands plus the chunk's decay vectors, 6.5 KB).
+constexpr int SCAN_KH_FLOATS = 8192;
+constexpr int SCAN_SLOT_FLOATS = 1664;
 size_t scan_workspace_bytes(const gdn_shape &s);
 
 // The layer path with fp16 inputs forms v inside the chunk kernel, from the

@@ -146,9 +146,9 @@ int gdn_pre(const gdn_shape *shape, const int32_t *cu_seqlens,
  *   alpha = exp(g[t][h])
  *   S <- alpha*S + beta[t][h] * (vc[t][h] - alpha*S kn[t][j]) kn[t][j]^T
  *   o[t][h] = S qn[t][j] / sqrt(dk)
- * The kernels evaluate this exactly (up to fp32 rounding) in 16-token chunks
+ * The kernels evaluate this exactly (up to fp32 rounding) in 32-token chunks
  * counted from each sequence's first token.  Splitting a sequence across calls
- * at a multiple of 16 tokens is therefore bit-identical to one call; any other
+ * at a multiple of 32 tokens is therefore bit-identical to one call; any other
  * split agrees within fp32 rounding.
  * In:  cu_seqlens, qn, kn, vc, g, beta; state (read: S at the start).
  * Out: o; state (overwritten in place with S after the last token).
@@ -162,8 +162,8 @@ int gdn_scan(const gdn_shape *shape, const int32_t *cu_seqlens,
              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of scratch gdn_scan needs for `shape` (0 if the shape is invalid):
- * (total_T/16 + n_seq + 1) slots, each holding hk key-head parts of 24 KB and
- * hv value-head parts of 2304 bytes. */
+ * (total_T/32 + n_seq + 1) slots, each holding hk key-head parts of 32 KB and
+ * hv value-head parts of 6656 bytes. */
 size_t gdn_scan_workspace_bytes(const gdn_shape *shape);
 
 /*

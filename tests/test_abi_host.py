@@ -47,8 +47,8 @@ def test_workspace_bytes():
     s = shape(total_T=2048, max_T=2048)
     T = 2048
     r = lambda x: (x + 255) // 256 * 256
-    per_slot = 16 * 24576 + 48 * 2304   # per 16-token chunk: key-head and value-head parts
-    scan = (T // 16 + 1 + 1) * per_slot
+    per_slot = 16 * 32768 + 48 * 6656   # per 32-token chunk: key-head and value-head parts
+    scan = (T // 32 + 1 + 1) * per_slot
     assert B.gdn_scan_workspace_bytes(s) == scan
     # fused fp16 path (3 value heads per key head): o and the scan scratch only
     assert B.gdn_prefill_workspace_bytes(s) == r(T * 48 * 128 * 4) + r(scan)
@@ -57,14 +57,14 @@ def test_workspace_bytes():
     assert B.gdn_prefill_workspace_bytes(s32) == 2 * r(T * 48 * 128 * 4) + r(scan)
     # staged path (more than 8 value heads per key head): every intermediate
     st = shape(hk=1, hv=10, total_T=2048, max_T=2048)
-    scan10 = (T // 16 + 2) * (24576 + 10 * 2304)
+    scan10 = (T // 32 + 2) * (32768 + 10 * 6656)
     want = 2 * r(T * 128 * 4) + r(T * 10 * 128 * 4) * 2 + 2 * r(T * 10 * 4) + r(scan10)
     assert B.gdn_prefill_workspace_bytes(st) == want
     assert B.gdn_prefill_workspace_bytes(shape(hv=47)) == 0
     assert B.gdn_scan_workspace_bytes(shape(hv=47)) == 0
-    # varlen: at most total_T / 16 + n_seq slots per value head
+    # varlen: at most total_T / 32 + n_seq slots per value head
     v = shape(n_seq=4, total_T=27135, max_T=16384)
-    assert B.gdn_scan_workspace_bytes(v) == (27135 // 16 + 4 + 1) * per_slot
+    assert B.gdn_scan_workspace_bytes(v) == (27135 // 32 + 4 + 1) * per_slot
 
 
 def _pre(s, **over):

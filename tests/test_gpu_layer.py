@@ -8,7 +8,7 @@ packed with another, graph replays of the layer equal to the eager call, key
 heads shared by 8 and 10 value heads, and split invariance of the path ("Round 30
 Track C Audit: gdn_pre, gdn_post, and gdn_scanr_4", section 2: the
 token-blocked scan must equal the single pass) -- bitwise for splits on the
-16-token chunk grid, within tolerance for any other split.
+32-token chunk grid, within tolerance for any other split.
 """
 import numpy as np
 import pytest
@@ -97,12 +97,12 @@ def test_continuation_split_matches_whole_and_oracle(gpu):
 
 
 def test_split_on_chunk_boundaries_is_bitwise(gpu):
-    # splits at multiples of 16 tokens keep the chunk grid: bit-identical
+    # splits at multiples of 32 tokens keep the chunk grid: bit-identical
     w = W["prod_continuation_fp16"]
     inp = synth.layer_inputs(w)
     banner("gdn_prefill_layer", w.name, "whole")
     whole = _run_layer(w, inp)
-    y, state, hist = _run_segments(w, inp, (16, 48, 272, 1024, 5))
+    y, state, hist = _run_segments(w, inp, (32, 64, 256, 992, 21))
     assert np.array_equal(y.view(np.uint16), np_(whole.y).view(np.uint16))
     assert np.array_equal(state.view(np.uint32), np_(whole.state).view(np.uint32))
     assert np.array_equal(hist.view(np.uint16), np_(whole.hist).view(np.uint16))
