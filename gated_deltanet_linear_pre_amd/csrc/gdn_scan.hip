@@ -39,8 +39,9 @@
 //     laid out in the exact per-lane operand order of the chunk kernel's
 //     MFMAs ("key-head slot", 32 KB per chunk); the same split operands give
 //     the chunk's k.k and k.q tiles on MFMA, once per key head;
-//   - per value head: the decays, T = (I + A)^-1 by forward substitution
-//     (one column per lane), M, Lam, beta and the last-row decays, T and M
+//   - per value head: the decays, T = (I + A)^-1 (its two diagonal blocks by
+//     forward substitution, one column per lane, and the off-diagonal block
+//     as a product), M, Lam, beta and the last-row decays, T and M
 //     split and laid out as MFMA operands ("value-head slot", 6.5 KB).
 // * chunk kernel (sequential over chunks): a block owns 32 value channels
 //   of one (sequence, value head) in two row groups of 16; each row group's
@@ -315,6 +316,13 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
     auto &sA = sm.u.at.sA[wave];
     auto &sT = sm.u.at.sT[wave];
     for (int gh = wave; gh < d.G; gh += 4) {
+        // lane index and chunk length made opaque to the compiler here, so
+        // that the many comparisons below are formed next to their use in
+        // every iteration rather than hoisted out of the loop and kept live
+        // (which spilled scalar registers)
+        int lane_o = lane, nv_o = nv;
+        __asm__ volatile("" : "+v"(lane_o), "+s"(nv_o));
+        const int l16 = lane_o & 15, kk = lane_o >> 4;
         const int h = j * d.G + gh;
         float *vs = ws + d.vh_base + (slot * hv + h) * SCAN_SLOT_FLOATS;
         const float g_own = g_next, b_own = b_next;
@@ -334,73 +342,67 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             const f4 x = *reinterpret_cast<const f4 *>(&sm.sGB[wave][0][4 * i]);
             gv[4 * i] = x[0]; gv[4 * i + 1] = x[1]; gv[4 * i + 2] = x[2]; gv[4 * i + 3] = x[3];
         }
-        // g and beta of tokens 4 kk .. 4 kk + 3 and 16 + 4 kk .. 16 + 4 kk + 3
-        const f4 g4a = *reinterpret_cast<const f4 *>(&sm.sGB[wave][0][4 * kk]);
-        const f4 g4b = *reinterpret_cast<const f4 *>(&sm.sGB[wave][0][16 + 4 * kk]);
+        // beta of tokens 4 kk .. 4 kk + 3 and 16 + 4 kk .. 16 + 4 kk + 3
         const f4 b4a = *reinterpret_cast<const f4 *>(&sm.sGB[wave][1][4 * kk]);
         const f4 b4b = *reinterpret_cast<const f4 *>(&sm.sGB[wave][1][16 + 4 * kk]);
-        // sum of g over (lo, hi]: one trip for every lane, per-lane bounds
-        auto gsum = [&](int lo, int hi) {
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 1; r < CT; ++r) acc += (r > lo && r <= hi) ? gv[r] : 0.f;
-            return acc;
-        };
-        // Every decay is the exp of a direct sum of the log decays it spans.
-        // A[t][s] = beta_t D[t][s] k_t.k_s (s < t), by tiles: lane (l16, kk)
-        // takes column s = l16 (+ 16) and rows t = 4 kk + i (+ 16), summing g
-        // over (s, t] once for i = 0 and then one more term per row.
+        // Every decay is the exp of a direct sum of the log decays it spans,
+        // summed in token order: lane s < 32 walks its column, D[t][s] =
+        // exp(g_{s+1} + ... + g_t) for t > s (1 on the diagonal, 0 above),
+        // into sT (free until T is formed); lane 32 + s the prefix sums from
+        // the chunk start, Lam_t = exp(g_0 + ... + g_t).  D[last][s] comes
+        // out of the same walk.
         {
-            // tile (0, 0): t = 4 kk + i, s = l16
-            float acc = gsum(l16, 4 * kk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * kk + i, s = l16;
-                if (i > 0) acc += t > s ? g4a[i] : 0.f;
-                sA[t][s] = (t < nv && s < t) ? b4a[i] * exp_fast(acc) * tl[0][i] : 0.f;
+            const int s = lane_o & 31;
+            const bool pref = lane_o >= 32;
+            float acc = pref ? gv[0] : 0.f;
+            float dl = (!pref && s == nv_o - 1) ? 1.f : 0.f;  // D[last][s]
+            if (!pref) sT[0][s] = s == 0 ? 1.f : 0.f;
+            else if (s == 0) {
+                vs[VH_LAM] = nv_o > 0 ? exp_fast(acc) * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
+                if (nv_o == 1) vs[VH_LAST] = expf(acc);
             }
-            // tile (1, 0): t = 16 + 4 kk + i, s = l16 (s < t always)
-            acc = gsum(l16, 16 + 4 * kk);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 + 4 * kk + i, s = l16;
-                if (i > 0) acc += g4b[i];
-                sA[t][s] = t < nv ? b4b[i] * exp_fast(acc) * tl[1][i] : 0.f;
+            for (int t = 1; t < CT; ++t) {
+                acc += (pref || t > s) ? gv[t] : 0.f;
+                const float e = exp_fast(acc);
+                if (!pref) {
+                    sT[t][s] = t > s ? e : t == s ? 1.f : 0.f;
+                    if (t == nv_o - 1 && t > s) dl = e;
+                } else if (s == t) {
+                    vs[VH_LAM + t] = t < nv_o ? e * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
+                    if (t == nv_o - 1) vs[VH_LAST] = expf(acc);
+                }
             }
-            // tile (1, 1): t = 16 + 4 kk + i, s = 16 + l16
-            acc = gsum(16 + l16, 16 + 4 * kk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 + 4 * kk + i, s = 16 + l16;
-                if (i > 0) acc += t > s ? g4b[i] : 0.f;
-                sA[t][s] = (t < nv && s < t) ? b4b[i] * exp_fast(acc) * tl[2][i] : 0.f;
+            if (!pref) {
+                vs[VH_BETA + s] = b_own;
+                vs[VH_W + s] = s < nv_o ? dl : 0.f;
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // A[t][s] = beta_t D[t][s] k_t.k_s (s < t), by tiles: lane (l16, kk)
+        // takes column s = l16 (+ 16) and rows t = 4 kk + i (+ 16)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t0 = 4 * kk + i, t1 = 16 + 4 * kk + i;
+            sA[t0][l16] = (t0 < nv_o && l16 < t0) ? b4a[i] * sT[t0][l16] * tl[0][i] : 0.f;
+            sA[t1][l16] = t1 < nv_o ? b4b[i] * sT[t1][l16] * tl[1][i] : 0.f;
+            sA[t1][16 + l16] = (t1 < nv_o && 16 + l16 < t1) ? b4b[i] * sT[t1][16 + l16] * tl[2][i] : 0.f;
+        }
         // M[t][s] = D[t][s] q_t.k_s (s <= t) in operand order, lane L = 16 kk + t':
-        //   M00: t = t', s = 4 kk + e;  M1: t = 16 + t', s = 16 (e / 4) + 4 kk + e % 4;
-        // the sum over (4 kk + 3, t] first, then one term per step down in s
+        //   M00: t = t', s = 4 kk + e;  M1: t = 16 + t', s = 16 (e / 4) + 4 kk + e % 4
         {
             const int tp = l16;
+            const f4 d00 = *reinterpret_cast<const f4 *>(&sT[tp][4 * kk]);
+            const f4 d1a = *reinterpret_cast<const f4 *>(&sT[16 + tp][4 * kk]);
+            const f4 d1b = *reinterpret_cast<const f4 *>(&sT[16 + tp][16 + 4 * kk]);
             f4 m00, m1a, m1b;
-            float acc = gsum(4 * kk + 3, tp);
 #pragma unroll
-            for (int e = 3; e >= 0; --e) {
-                const int s = 4 * kk + e;
-                if (e < 3) acc += (s + 1 <= tp) ? g4a[e + 1] : 0.f;
-                m00[e] = (tp < nv && s <= tp) ? exp_fast(acc) * tl[3][e] : 0.f;
-            }
-            acc = gsum(4 * kk + 3, 16 + tp);
-#pragma unroll
-            for (int e = 3; e >= 0; --e) {
-                if (e < 3) acc += g4a[e + 1];
-                m1a[e] = 16 + tp < nv ? exp_fast(acc) * tl[4][e] : 0.f;
-            }
-            acc = gsum(16 + 4 * kk + 3, 16 + tp);
-#pragma unroll
-            for (int e = 3; e >= 0; --e) {
-                const int s = 16 + 4 * kk + e;
-                if (e < 3) acc += (s + 1 <= 16 + tp) ? g4b[e + 1] : 0.f;
-                m1b[e] = (16 + tp < nv && s <= 16 + tp) ? exp_fast(acc) * tl[5][e] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                m00[e] = tp < nv_o ? d00[e] * tl[3][e] : 0.f;
+                m1a[e] = 16 + tp < nv_o ? d1a[e] * tl[4][e] : 0.f;
+                m1b[e] = 16 + tp < nv_o ? d1b[e] * tl[5][e] : 0.f;
             }
             h4 hi, lo;
             split4<false>(m00, hi, lo, d.m1);
@@ -411,50 +413,53 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             *reinterpret_cast<h8 *>(mp + 512 + lane * 8) = h1;
             *reinterpret_cast<h8 *>(mp + 1024 + lane * 8) = l1;
         }
-        if (lane < CT) {
-            const int t = lane;
-            float lam = 0.f, wdec = 0.f;
-#pragma unroll
-            for (int r = 0; r < CT; ++r) {
-                lam += r <= t ? gv[r] : 0.f;
-                wdec += (r > t && r < nv) ? gv[r] : 0.f;
-            }
-            // Lam_t and D[last][t] weight this chunk's terms only; Lam_last
-            // multiplies the whole state every chunk, so it takes the
-            // correctly rounded exp
-            vs[VH_LAM + t] = t < nv ? exp_fast(lam) * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
-            vs[VH_BETA + t] = b_own;
-            vs[VH_W + t] = t < nv ? exp_fast(wdec) : 0.f;
-            if (t == nv - 1) vs[VH_LAST] = expf(lam);
-        }
         // the wave's A writes must land before its lanes read them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < CT) {
-            // T = (I + A)^-1 by forward substitution; lane s keeps column s.
-            // Rows of A are read four entries at a time (the same address on
-            // every lane); entries at or right of the diagonal are not used.
-            const int s = lane;
-            float Tc[CT];
+        {
+            // T = (I + A)^-1 by blocks: T00 = (I + A00)^-1 and T11 = (I + A11)^-1
+            // by forward substitution at once (lane s < 16 keeps column s of
+            // T00, lane 16 + s column s of T11; rows of A read four entries at
+            // a time, entries at or right of the diagonal unused), then
+            // T10 = -T11 A10 T00.
+            if (lane < CT) {
+                const int o = lane & 16, s = lane & 15;
+                float Tc[16];
 #pragma unroll
-            for (int t = 0; t < CT; ++t) {
-                float acc[4] = {(t == s) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 16; ++t) {
+                    float acc[4] = {(t == s) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r4 = 0; r4 < t; r4 += 4) {
-                    const f4 a = *reinterpret_cast<const f4 *>(&sA[t][r4]);
+                    for (int r4 = 0; r4 < t; r4 += 4) {
+                        const f4 a = *reinterpret_cast<const f4 *>(&sA[o + t][o + r4]);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (r4 + q < t) acc[q] = fmaf(-a[q], Tc[r4 + q], acc[q]);
+                        for (int q = 0; q < 4; ++q)
+                            if (r4 + q < t) acc[q] = fmaf(-a[q], Tc[r4 + q], acc[q]);
+                    }
+                    Tc[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
                 }
-                Tc[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            }
 #pragma unroll
-            for (int t = 0; t < CT; ++t) sT[t][s] = Tc[t];
+                for (int t = 0; t < 16; ++t) sT[o + t][o + s] = Tc[t];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // fp32 MFMA 16x16x4 (lane (l16, kk) gives A[l16][kk], B[kk][l16] per
+            // 4-deep step i), over the contraction order k = 4 kk + i so that
+            // the first product's accumulator layout (W[4 kk + r][l16] in
+            // component r) is the second's B operand as it stands:
+            //   W = A10 T00,  T10 = -(T11 W)
+            f4 W = z4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                W = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 + l16][4 * kk + i], sT[4 * kk + i][l16], W, 0, 0, 0);
+            f4 T10 = z4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[16 + l16][16 + 4 * kk + i], W[i], T10, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[16 + 4 * kk + r][l16] = -T10[r];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         {
             // T in operand order, lane L = 16 kk + t':
             //   T00 (hi | lo): T[t'][4 kk + e];  T1: T[16 + t'][16 (e / 4) + 4 kk + e % 4]
