@@ -154,6 +154,10 @@ def main():
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--legs", default="prefill,staged,varlen,decode",
+                    help="comma-separated subset of prefill (the layer path, the headline), staged "
+                         "(gdn_pre, gdn_scan, gdn_post; the roofline), varlen (the long varlen "
+                         "batch) and decode; a profiler run can take one workload at a time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (for scaling the HBM "
                          "byte counters of a profiler run)")
@@ -282,14 +286,22 @@ def main():
             per[name] = timed(fn, steps) / L
         return dict(ms_per_step=total_ms, pre_ms=per["pre"], scan_ms=per["scan"], post_ms=per["post"])
 
-    log("timing the layer path, fp16 output")
-    l16 = run_layer("f16", args.steps, args.warmup)
-    log("timing the layer path, fp32 output")
-    l32 = run_layer("f32", args.steps, args.warmup)
-    log("timing the staged path (per-stage events), fp16 output")
-    r16 = run("f16", args.steps, args.warmup)
-    log("timing the staged path, fp32 output")
-    r32 = run("f32", args.steps, args.warmup)
+    legs = set(args.legs.split(","))
+    if "prefill" in legs:
+        log("timing the layer path, fp16 output")
+        l16 = run_layer("f16", args.steps, args.warmup)
+        log("timing the layer path, fp32 output")
+        l32 = run_layer("f32", args.steps, args.warmup)
+    else:
+        l16 = l32 = {"ms_per_step": float("nan")}
+    if "staged" in legs:
+        log("timing the staged path (per-stage events), fp16 output")
+        r16 = run("f16", args.steps, args.warmup)
+        log("timing the staged path, fp32 output")
+        r32 = run("f32", args.steps, args.warmup)
+    else:
+        nan = float("nan")
+        r16 = r32 = dict(ms_per_step=nan, pre_ms=nan, scan_ms=nan, post_ms=nan)
 
     scan_s = r16["scan_ms"] / 1e3
     achieved_tf = scan_flops(T, hv) / scan_s / 1e12
@@ -435,11 +447,15 @@ def main():
                 "critical_path_chunk_steps": (max(wv.seqlens) + 15) // 16,
                 "cpu_baseline": None}
 
-    log("timing the long varlen batch (36 layers, T = 16384 + 8192 + 2048 + 511)")
-    var = varlen(max(3, args.steps // 4), 1)
+    var = None
+    if "varlen" in legs:
+        log("timing the long varlen batch (36 layers, T = 16384 + 8192 + 2048 + 511)")
+        var = varlen(max(3, args.steps // 4), 1)
 
-    log("timing gdn_step decode")
-    dec = [decode(b) for b in (1, 8, 64)]
+    dec = None
+    if "decode" in legs:
+        log("timing gdn_step decode")
+        dec = [decode(b) for b in (1, 8, 64)]
 
     res = {
         "metric": METRIC,
@@ -471,8 +487,9 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host cores")
         res["cpu_baseline"] = cpu_baseline()
-        log("timing the fp64 oracle on one layer of the long varlen batch")
-        res["varlen4"]["cpu_baseline"] = cpu_baseline_varlen()
+        if var is not None:
+            log("timing the fp64 oracle on one layer of the long varlen batch")
+            res["varlen4"]["cpu_baseline"] = cpu_baseline_varlen()
     print(json.dumps(res), flush=True)
 
 

@@ -347,40 +347,43 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
         const f4 b4b = *reinterpret_cast<const f4 *>(&sm.sGB[wave][1][16 + 4 * kk]);
         // Every decay is the exp of a direct sum of the log decays it spans,
         // summed in token order: lane s < 32 walks its column, D[t][s] =
-        // exp(g_{s+1} + ... + g_t) for t > s (1 on the diagonal, 0 above),
-        // into sT (free until T is formed); lane 32 + s the prefix sums from
-        // the chunk start, Lam_t = exp(g_0 + ... + g_t).  D[last][s] comes
-        // out of the same walk.
+        // exp(g_{s+1} + ... + g_t) for t > s (0 above the diagonal, and 1 on
+        // it, written after the walk), into sT (free until T is formed);
+        // lanes 32.. take the prefix sums from the chunk start, into sT's
+        // padding columns: Lam_t = exp(g_0 + ... + g_t) in column 32, the sum
+        // itself in column 33.  The walk has no comparison: whether token t
+        // counts for column s is the sign of s - t.
         {
             const int s = lane_o & 31;
             const bool pref = lane_o >= 32;
-            float acc = pref ? gv[0] : 0.f;
-            float dl = (!pref && s == nv_o - 1) ? 1.f : 0.f;  // D[last][s]
-            if (!pref) sT[0][s] = s == 0 ? 1.f : 0.f;
-            else if (s == 0) {
-                vs[VH_LAM] = nv_o > 0 ? exp_fast(acc) * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
-                if (nv_o == 1) vs[VH_LAST] = expf(acc);
-            }
+            const int colw = pref ? (lane_o >= 48 ? 33 : 32) : s;
+            const uint32_t allm = pref ? 0xffffffffu : 0u;
+            const bool wsum = lane_o >= 48;
+            float acc = 0.f;
 #pragma unroll
-            for (int t = 1; t < CT; ++t) {
-                acc += (pref || t > s) ? gv[t] : 0.f;
+            for (int t = 0; t < CT; ++t) {
+                const uint32_t m = (uint32_t)((s - t) >> 31) | allm;  // all ones if t counts
+                acc += __uint_as_float(__float_as_uint(gv[t]) & m);
                 const float e = exp_fast(acc);
-                if (!pref) {
-                    sT[t][s] = t > s ? e : t == s ? 1.f : 0.f;
-                    if (t == nv_o - 1 && t > s) dl = e;
-                } else if (s == t) {
-                    vs[VH_LAM + t] = t < nv_o ? e * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
-                    if (t == nv_o - 1) vs[VH_LAST] = expf(acc);
-                }
+                sT[t][colw] = __uint_as_float(__float_as_uint(wsum ? acc : e) & m);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (!pref) sT[s][s] = 1.f;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (!pref) {
+                // Lam_t and D[last][t] weight this chunk's terms only
+                vs[VH_LAM + s] = s < nv_o ? sT[s][32] * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
                 vs[VH_BETA + s] = b_own;
-                vs[VH_W + s] = s < nv_o ? dl : 0.f;
+                vs[VH_W + s] = s < nv_o ? sT[nv_o - 1][s] : 0.f;
             }
+            // Lam_last multiplies the whole state every chunk, so it takes
+            // the correctly rounded exp
+            if (lane_o == 32) vs[VH_LAST] = expf(sT[nv_o - 1][33]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // A[t][s] = beta_t D[t][s] k_t.k_s (s < t), by tiles: lane (l16, kk)
         // takes column s = l16 (+ 16) and rows t = 4 kk + i (+ 16)
 #pragma unroll
@@ -789,6 +792,9 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         side_barrier();
         for (int c = 0; c < n_chunks; ++c) {
             side_barrier();
+            // let the compute waves' reads that the recurrence waits for
+            // reach the LDS first (~512 cycles)
+            __builtin_amdgcn_s_sleep(8);
             if (c > 0) o_store(c - 1);
             take_lam_m(c);
         }
@@ -949,8 +955,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 
         // Reads in the order they are needed, since each wave's LDS reads
         // complete in order and four waves read at once after the barrier:
-        // the partner's partial P, this chunk's value-head operands and v,
-        // and K^T for the update; Q and the next chunk's K once U is formed.
+        // what B needs (the partner's partial P, Lam, beta, v); then T, the
+        // last-row decays and K^T; Q and the next chunk's K once U is formed.
         const f4 Po0 = sXP[x][partner][0][lane];
         const f4 Po1 = sXP[x][partner][1][lane];
         const f4 lam0 = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
@@ -962,6 +968,17 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         for (int r = 0; r < 4; ++r) {
             vv0[r] = sV[x][4 * kk + r][grp * 16 + l16];
             vv1[r] = sV[x][16 + 4 * kk + r][grp * 16 + l16];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the full P, summed in the same order by both waves of the pair;
+        // B = beta (V - Lam P), component r is token 16 tau + 4 kk + r, channel l16
+        const f4 P0 = kh == 0 ? Pp[0] + Po0 : Po0 + Pp[0];
+        const f4 P1 = kh == 0 ? Pp[1] + Po1 : Po1 + Pp[1];
+        f4 B0, B1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            B0[r] = bet0[r] * __builtin_fmaf(-lam0[r], P0[r], vv0[r]);
+            B1[r] = bet1[r] * __builtin_fmaf(-lam1[r], P1[r], vv1[r]);
         }
         const _Float16 *tpp = reinterpret_cast<const _Float16 *>(vh + VH_TP);
         const h8 tp0 = *reinterpret_cast<const h8 *>(tpp + lane * 8);
@@ -977,18 +994,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
             for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
                 for (int tau = 0; tau < 2; ++tau) kt[b][hl][tau] = kt_half(sKP[kb_cur], b, hl, tau);
-        __builtin_amdgcn_sched_barrier(0);  // the reads go out before the work below
+        __builtin_amdgcn_sched_barrier(0);
 
-        // the full P, summed in the same order by both waves of the pair;
-        // B = beta (V - Lam P), component r is token 16 tau + 4 kk + r, channel l16
-        const f4 P0 = kh == 0 ? Pp[0] + Po0 : Po0 + Pp[0];
-        const f4 P1 = kh == 0 ? Pp[1] + Po1 : Po1 + Pp[1];
-        f4 B0, B1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            B0[r] = bet0[r] * __builtin_fmaf(-lam0[r], P0[r], vv0[r]);
-            B1[r] = bet1[r] * __builtin_fmaf(-lam1[r], P1[r], vv1[r]);
-        }
         h4 bh0, bl0, bh1, bl1;
         split4<true>(B0, bh0, bl0, d.ms);
         split4<true>(B1, bh1, bl1, d.ms);
