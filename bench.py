@@ -128,6 +128,23 @@ def cpu_baseline(budget_s=12.0, layers_total=36):
                           "sample": "layer 0, T=2048, all 48 value heads, 1 thread, scaled to 36 layers"})
 
 
+def chunk_step_schedule(seqlens, hv, n_cu, chunk=32, blocks_per_head=4):
+    """Chunk steps on the longest sequence's chain, and the makespan of the
+    chunk kernel's blocks dealt longest sequence first to n_cu CUs, one block
+    per CU at a time (its LDS use), each block running ceil(len / chunk) steps."""
+    import heapq
+    lens = sorted(seqlens, reverse=True)
+    free = [0] * n_cu
+    for L_ in lens:
+        for _ in range(hv * blocks_per_head):
+            t = heapq.heappop(free)
+            heapq.heappush(free, t + (L_ + chunk - 1) // chunk)
+    crit = (lens[0] + chunk - 1) // chunk
+    work = sum(hv * blocks_per_head * ((L_ + chunk - 1) // chunk) for L_ in lens)
+    return {"critical_path": crit, "list_schedule_makespan": max(free),
+            "work_over_cus": round(work / n_cu, 1)}
+
+
 def cpu_baseline_varlen(layers_total=36):
     """The fp64 oracle on one whole layer of the long varlen batch (layer 0:
     all four sequences, all 48 value heads), extrapolated to 36 layers."""
@@ -444,7 +461,8 @@ def main():
                              "achieved": round(tf, 3), "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4), "us_per_call": round(scan_us, 1),
                              "flops_per_launch": scan_flops(Tv, hv)},
-                "critical_path_chunk_steps": (max(wv.seqlens) + 15) // 16,
+                "chunk_steps": chunk_step_schedule(wv.seqlens, hv,
+                                                   torch.cuda.get_device_properties(dev).multi_processor_count),
                 "cpu_baseline": None}
 
     var = None
