@@ -99,12 +99,25 @@ constexpr float KQ_SCALE = 16.f; // k and q scale before the fp16 split (exact)
 constexpr float SCALE = 0.08838834764831845f;  // 1 / sqrt(128)
 
 // key-head slot, in fp16 elements: K, then Q, each
-// [2 token tiles][4 key steps][2 hi/lo][64 lanes][8]; lane 16 kk + t of tile
-// tau, key step s holds keys 32 s + 16 (e / 4) + 4 kk + e % 4 of token 16 tau + t
+// [2 token tiles][4 key steps][2 hi/lo][64 positions][8]; lane 16 kk + t of
+// tile tau, key step s holds keys 32 s + 16 (e / 4) + 4 kk + e % 4 of token
+// 16 tau + t, at position lane in Q and kpos(lane) in K.
 constexpr int KH_KP = 0;
 constexpr int KH_QP = 8192;
 static_assert(SCAN_KH_FLOATS * 2 == 16384, "key-head slot size");
 __host__ __device__ constexpr int kp_off(int tau, int s, int hl) { return ((tau * 4 + s) * 2 + hl) * 512; }
+// K's positions are swizzled for the transposing K^T read, whose 16 lanes of
+// a group address four tokens of all four key quads kk: unswizzled those sit
+// 256 bytes apart, on the same LDS banks (measured: 6 conflict cycles per
+// read).  Position 16 kk + (t ^ 4 x(kk)), x = (0, 3, 2, 1), spreads each
+// half-wave's 32 addresses over every 16-byte bank group twice (2 cycles,
+// the least for 8-byte reads that all take the same half of a 16-byte
+// piece), and keeps the 16-byte operand reads free of conflicts (measured;
+// the plain x(kk) = kk is not).
+__host__ __device__ constexpr int kpos(int lane)
+{
+    return lane ^ (4 * ((lane >> 4) ^ (((lane >> 4) & 1) << 1)));
+}
 // value-head slot, in floats
 constexpr int VH_TP = 0;       // [3][64 lanes][8] fp16: T00 (hi 4 | lo 4), T1 hi, T1 lo
 constexpr int VH_MP = 768;     // the same for M
@@ -280,8 +293,8 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             }
             split8<false>(ka, kb, khi[tau], klo[tau], d.m1);
             split8<false>(qa, qb, qhi[tau], qlo[tau], d.m1);
-            *reinterpret_cast<h8 *>(kh + KH_KP + kp_off(tau, s, 0) + lane * 8) = khi[tau];
-            *reinterpret_cast<h8 *>(kh + KH_KP + kp_off(tau, s, 1) + lane * 8) = klo[tau];
+            *reinterpret_cast<h8 *>(kh + KH_KP + kp_off(tau, s, 0) + kpos(lane) * 8) = khi[tau];
+            *reinterpret_cast<h8 *>(kh + KH_KP + kp_off(tau, s, 1) + kpos(lane) * 8) = klo[tau];
             *reinterpret_cast<h8 *>(kh + KH_QP + kp_off(tau, s, 0) + lane * 8) = qhi[tau];
             *reinterpret_cast<h8 *>(kh + KH_QP + kp_off(tau, s, 1) + lane * 8) = qlo[tau];
         }
@@ -894,16 +907,17 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 #pragma unroll
     for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b) * KQ_SCALE;
 
-    // this wave's two 32-key steps of K (or Q) of both token tiles, hi and lo
-    auto key_ops = [&](const float *base, h8 (&hi)[2][2], h8 (&lo)[2][2]) {
+    // this wave's two 32-key steps of K (pos = kpos(lane)) or Q (pos = lane)
+    // of both token tiles, hi and lo
+    auto key_ops = [&](const float *base, int pos, h8 (&hi)[2][2], h8 (&lo)[2][2]) {
         const _Float16 *kb = reinterpret_cast<const _Float16 *>(base);
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int s = 2 * kh + i;
-                hi[tau][i] = *reinterpret_cast<const h8 *>(kb + kp_off(tau, s, 0) + lane * 8);
-                lo[tau][i] = *reinterpret_cast<const h8 *>(kb + kp_off(tau, s, 1) + lane * 8);
+                hi[tau][i] = *reinterpret_cast<const h8 *>(kb + kp_off(tau, s, 0) + pos * 8);
+                lo[tau][i] = *reinterpret_cast<const h8 *>(kb + kp_off(tau, s, 1) + pos * 8);
             }
     };
     // K^T of key block b' = 4 kh + b (keys 16 b' .. + 15) from K's LDS copy
@@ -912,7 +926,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     // lane 4 jj + q addresses keys 16 b' + 4 q .. + 3 of token 16 tau + 4 kk +
     // jj, so lane (m, kk) receives K[16 tau + 4 kk + jj][16 b' + m]: the
     // update's A operand in the permuted token order.
-    const int tr_off = (16 * (l16 & 3) + 4 * kk + (l16 >> 2)) * 8;
+    const int tr_off = kpos(16 * (l16 & 3) + 4 * kk + (l16 >> 2)) * 8;
     auto kt_half = [&](const float *base, int b, int hl, int tau) -> h4 {
         const int bp = 4 * kh + b;
         const _Float16 *q = reinterpret_cast<const _Float16 *>(base) + kp_off(tau, bp >> 1, hl) + tr_off +
@@ -926,7 +940,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     // step to that of the next.
     lds_barrier();  // chunk 0's operands and chunk 1's K are in LDS
     h8 kph[2][2], kpl[2][2];
-    key_ops(sKP[0], kph, kpl);
+    key_ops(sKP[0], kpos(lane), kph, kpl);
     int kb_cur = 0;  // ring slot of this chunk's K (c % 3)
     for (int c = 0; c < n_chunks; ++c) {
         const int x = c & 1;
@@ -1022,8 +1036,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         // is may be given the registers of its operands, see tests/asm_hazards.py)
         __builtin_amdgcn_sched_barrier(0);
         h8 qph[2][2], qpl[2][2];
-        key_ops(qv, qph, qpl);
-        if (c + 1 < n_chunks) key_ops(sKP[kb_next], kph, kpl);
+        key_ops(qv, lane, qph, qpl);
+        if (c + 1 < n_chunks) key_ops(sKP[kb_next], kpos(lane), kph, kpl);
         __builtin_amdgcn_sched_barrier(0);
         // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U) over the 32 permuted
         // tokens: this wave's 4 key blocks, three split terms chained each
