@@ -935,22 +935,64 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     };
 
     // K of chunk c + 1 is read from LDS during step c (it landed before the
-    // barrier of step c), and the partial R of chunk c is formed after the
-    // state update of step c: neither is on the path from the barrier of one
-    // step to that of the next.
+    // barrier of step c).  The partial R = Q S^T of chunk c is formed at the
+    // start of step c + 1, its products beside the split of the updated
+    // state, from the split of the state before the update (kept) and Q of
+    // chunk c (read during step c); it reaches LDS before the barrier of step
+    // c + 1, where the output wave takes it.  Neither is on the path from the
+    // barrier of one step to that of the next.
     lds_barrier();  // chunk 0's operands and chunk 1's K are in LDS
     h8 kph[2][2], kpl[2][2];
     key_ops(sKP[0], kpos(lane), kph, kpl);
+    // Q of the previous chunk; zero before chunk 0, whose step stores a zero
+    // R into the exchange slot of chunk -1 (the slot of chunk 1, rewritten
+    // before anything reads it)
+    h8 qph[2][2], qpl[2][2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) qph[tau][i] = qpl[tau][i] = h8{};
+    // partial R = Q S^T (x256) of chunk cr from the split (shp, slp) of the
+    // state before its update
+    auto r_partial = [&](int cr, const h8 (&shp)[2], const h8 (&slp)[2]) {
+        const int xr = cr & 1;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            f4 Rhh = z4, Rhl = z4, Rlh = z4;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                Rhh = mfma_k32(qph[tau][i], shp[i], Rhh);
+                Rhl = mfma_k32(qph[tau][i], slp[i], Rhl);   // x LO_SCALE
+                Rlh = mfma_k32(qpl[tau][i], shp[i], Rlh);
+            }
+            sXR[xr][wave][tau][lane] = (Rhh + Rlh) + Rhl * LO_UNSCALE;
+        }
+    };
     int kb_cur = 0;  // ring slot of this chunk's K (c % 3)
-    for (int c = 0; c < n_chunks; ++c) {
+    // one chunk step: (sh, sl) receive the split of this chunk's state,
+    // (shp, slp) hold the previous chunk's
+    auto step = [&](int c, h8 (&sh)[2], h8 (&sl)[2], const h8 (&shp)[2], const h8 (&slp)[2]) {
         const int x = c & 1;
         const int kb_next = kb_cur == 2 ? 0 : kb_cur + 1;
         const float *qv = sQV[x];
         const float *vh = qv + KH_HALF_FLOATS;
         // partial P = K S^T (x256) over this wave's 64 keys, per token tile
-        h8 sh[2], sl[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) split8<true>(S4[2 * i], S4[2 * i + 1], sh[i], sl[i], d.ms);
+        // K^T of this chunk for the update, read now while the LDS is quiet
+        // (K landed before the previous barrier); after the split, which has
+        // taken the last products' results, so no product is in flight
+        __builtin_amdgcn_sched_barrier(0);
+        h4 kt[4][2][2];  // [key block][hi/lo][token tile]
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                for (int tau = 0; tau < 2; ++tau) kt[b][hl][tau] = kt_half(sKP[kb_cur], b, hl, tau);
+        __builtin_amdgcn_sched_barrier(0);
+        // the previous chunk's partial R
+        r_partial(c - 1, shp, slp);
         f4 Pp[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
@@ -969,8 +1011,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 
         // Reads in the order they are needed, since each wave's LDS reads
         // complete in order and four waves read at once after the barrier:
-        // what B needs (the partner's partial P, Lam, beta, v); then T, the
-        // last-row decays and K^T; Q and the next chunk's K once U is formed.
+        // what B needs (the partner's partial P, Lam, beta, v); then T and
+        // the last-row decays; Q and the next chunk's K once U is formed.
         const f4 Po0 = sXP[x][partner][0][lane];
         const f4 Po1 = sXP[x][partner][1][lane];
         const f4 lam0 = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
@@ -1001,13 +1043,6 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         const f4 wu0 = *reinterpret_cast<const f4 *>(vh + VH_W + 4 * kk);
         const f4 wu1 = *reinterpret_cast<const f4 *>(vh + VH_W + 16 + 4 * kk);
         const float last = vh[VH_LAST];
-        h4 kt[4][2][2];  // [key block][hi/lo][token tile]
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                for (int tau = 0; tau < 2; ++tau) kt[b][hl][tau] = kt_half(sKP[kb_cur], b, hl, tau);
         __builtin_amdgcn_sched_barrier(0);
 
         h4 bh0, bl0, bh1, bl1;
@@ -1035,7 +1070,6 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         // (here no product of this step is in flight: a load issued while one
         // is may be given the registers of its operands, see tests/asm_hazards.py)
         __builtin_amdgcn_sched_barrier(0);
-        h8 qph[2][2], qpl[2][2];
         key_ops(qv, lane, qph, qpl);
         if (c + 1 < n_chunks) key_ops(sKP[kb_next], kpos(lane), kph, kpl);
         __builtin_amdgcn_sched_barrier(0);
@@ -1049,20 +1083,21 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
             C = mfma_k32(ktl, uwh, C);
             S4[b] = mfma_k32(kth * (_Float16)LO_UNSCALE, uwl, C);
         }
-        // partial R = Q S^T (x256) of this chunk from the split of the state
-        // before the update; the output wave reads it after the next barrier
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            f4 Rhh = z4, Rhl = z4, Rlh = z4;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                Rhh = mfma_k32(qph[tau][i], sh[i], Rhh);
-                Rhl = mfma_k32(qph[tau][i], sl[i], Rhl);   // x LO_SCALE
-                Rlh = mfma_k32(qpl[tau][i], sh[i], Rlh);
-            }
-            sXR[x][wave][tau][lane] = (Rhh + Rlh) + Rhl * LO_UNSCALE;
-        }
         kb_cur = kb_next;
+    };
+    // two steps per turn, so that the two splits alternate between register
+    // sets instead of being copied
+    h8 shA[2] = {}, slA[2] = {}, shB[2] = {}, slB[2] = {};
+    int c = 0;
+    for (; c + 1 < n_chunks; c += 2) {
+        step(c, shA, slA, shB, slB);
+        step(c + 1, shB, slB, shA, slA);
+    }
+    if (c < n_chunks) {
+        step(c, shA, slA, shB, slB);
+        r_partial(c, shA, slA);
+    } else {
+        r_partial(c - 1, shB, slB);
     }
     lds_barrier();  // R and U of the last chunk are visible to the output wave
 #pragma unroll
