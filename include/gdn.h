@@ -29,7 +29,11 @@
  * caller owns every buffer.
  *
  * Return value: GDN_OK (0), or a negative gdn_status.  All argument checks
- * run before anything is enqueued, so on error nothing has been launched.
+ * run before anything is enqueued, so on an argument error nothing has been
+ * launched.  GDN_E_LAUNCH is the exception: a call that enqueues several
+ * kernels (gdn_scan, gdn_prefill_layer, gdn_step) returns it when the runtime
+ * refuses one of them, and the kernels before it stay enqueued; hist and
+ * state may then be partly overwritten and must be treated as undefined.
  * Errors of the asynchronous kernels themselves surface at the caller's next
  * synchronisation.  A call with total_T == 0 is a no-op that returns GDN_OK
  * (history and state unchanged).
@@ -150,6 +154,15 @@ int gdn_pre(const gdn_shape *shape, const int32_t *cu_seqlens,
  * counted from each sequence's first token.  Splitting a sequence across calls
  * at a multiple of 32 tokens is therefore bit-identical to one call; any other
  * split agrees within fp32 rounding.
+ * Numerical domain: the products run on fp16 matrix cores with each fp32
+ * operand split into a high and a low fp16 half (about 22 significant bits),
+ * the low halves of the data-scaled operands carried x 2^10.  Accuracy holds
+ * while 16*|S|, |beta (v - alpha-weighted S k)| and the chunk's write vectors
+ * stay below 65504 (in practice |S| up to a few thousand, |v| up to ~6e4);
+ * past that a low half overflows and the results turn non-finite, which the
+ * output shows.  On the small side a split operand keeps its ~22 bits down
+ * to |x| near 2^-13, below which its error is an absolute floor near 2^-34;
+ * states whose RMS is above ~1e-6 hold 2e-4 of their RMS elementwise.
  * In:  cu_seqlens, qn, kn, vc, g, beta; state (read: S at the start).
  * Out: o; state (overwritten in place with S after the last token).
  * workspace: device scratch of >= gdn_scan_workspace_bytes(shape) bytes,
@@ -180,8 +193,9 @@ int gdn_post(const gdn_shape *shape, const float *o, const void *z,
              const void *gamma, void *y, void *stream);
 
 /* Bytes of workspace gdn_prefill_layer needs for `shape` (0 if the shape is
- * invalid): room for qn, kn, vc, g, beta, o and the scan scratch, each
- * 256-byte aligned. */
+ * invalid), by the path the shape takes, each part 256-byte aligned: o and
+ * the scan scratch always; with fp32 io and hv/hk <= 8 also vc; with
+ * hv/hk > 8 (the three stages in turn) also qn, kn, vc, g and beta. */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
 
 /*
