@@ -582,7 +582,6 @@ constexpr int COPY_WAVE = 4, OUT_WAVE = 5, V_WAVE = 7;
 constexpr int chunk_threads(bool raw_v) { return 64 * (raw_v ? 8 : 7); }
 constexpr int CHUNK_ROWS = 32;                       // value channels per block
 constexpr int KH_HALF_FLOATS = SCAN_KH_FLOATS / 2;   // K (or Q) of one key-head slot, in floats
-constexpr int QV_FLOATS = KH_HALF_FLOATS + SCAN_SLOT_FLOATS;  // Q + the value-head slot
 
 // Block-wide barrier ordering LDS only: global copies in flight stay in flight.
 __device__ __forceinline__ void lds_barrier()
@@ -608,14 +607,14 @@ __device__ __forceinline__ void side_barrier()
 }
 
 // LDS rings: chunk c's K in sKP[c % 3] (read a step ahead for K S^T, and as
-// K^T in step c); its Q and value-head slot in sQV[c % 2]; with RAW_V its raw
+// K^T in step c); its value-head slot in sVH[c % 2]; with RAW_V its raw
 // fp16 v rows in sRaw[c % 3]; its fp32 v in sV[c % 2].
 template <bool RAW_V>
 __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanArgs p, ChunkDims d,
                                                                          VRawArgs vr)
 {
     __shared__ __attribute__((aligned(16))) float sKP[3][KH_HALF_FLOATS];
-    __shared__ __attribute__((aligned(16))) float sQV[2][QV_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sVH[2][SCAN_SLOT_FLOATS];
     constexpr int RAW_BUF = RAW_V ? 3 : 1;
     __shared__ __attribute__((aligned(16))) _Float16 sRaw[RAW_BUF][CT][CHUNK_ROWS];
     __shared__ __attribute__((aligned(16))) _Float16 sRawH[3][CHUNK_ROWS];
@@ -682,18 +681,15 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 #pragma unroll
             for (int m = 0; m < K_PIECES; ++m) copy16(src + m * 256, dst + m * 256);
         };
-        auto issue_qv = [&](int c) {
+        auto issue_vh = [&](int c) {
             const int b = c & 1;
-            const float *src = kh_src(c) + KH_HALF_FLOATS + lane * 4;
-#pragma unroll
-            for (int m = 0; m < K_PIECES; ++m) copy16(src + m * 256, &sQV[b][m * 256]);
             const float *vhs = p.ws + d.vh_base + (chunk_slot(cu0, n, c) * hv + h) * SCAN_SLOT_FLOATS;
 #pragma unroll
             for (int m = 0; m < VH_PIECES; ++m)
-                copy16(vhs + m * 256 + lane * 4, &sQV[b][KH_HALF_FLOATS + m * 256]);
+                copy16(vhs + m * 256 + lane * 4, &sVH[b][m * 256]);
             // the last 512 bytes: two dword copies
-            copy4(vhs + VH_PIECES * 256 + lane, &sQV[b][KH_HALF_FLOATS + VH_PIECES * 256]);
-            copy4(vhs + VH_PIECES * 256 + 64 + lane, &sQV[b][KH_HALF_FLOATS + VH_PIECES * 256 + 64]);
+            copy4(vhs + VH_PIECES * 256 + lane, &sVH[b][VH_PIECES * 256]);
+            copy4(vhs + VH_PIECES * 256 + 64 + lane, &sVH[b][VH_PIECES * 256 + 64]);
             if constexpr (!RAW_V) {
                 // fp32 v: lane l takes token 8 m + l / 8, channels 4 (l % 8) .. + 3
                 const int64_t tb = (int64_t)cu0 + (int64_t)c * CT;
@@ -724,12 +720,12 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         };
         // Issued after the barrier of step c (the compute waves are then done
         // with chunk c - 1), waited for before that of step c + 1: chunk
-        // c + 2's K (read during step c + 1), chunk c + 1's Q, value-head slot
+        // c + 2's K (read during step c + 1), chunk c + 1's value-head slot
         // and fp32 v, and with RAW_V chunk c + 2's raw rows (the v wave turns
         // them into v between the barriers of steps c + 1 and c + 2).
         issue_k(0);
         if (n_chunks > 1) issue_k(1);
-        issue_qv(0);
+        issue_vh(0);
         issue_raw(0);
         if (n_chunks > 1) issue_raw(1);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -737,7 +733,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         for (int c = 0; c < n_chunks; ++c) {
             side_barrier();
             if (c + 2 < n_chunks) issue_k(c + 2);
-            if (c + 1 < n_chunks) issue_qv(c + 1);
+            if (c + 1 < n_chunks) issue_vh(c + 1);
             if (c + 2 < n_chunks) issue_raw(c + 2);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
@@ -756,7 +752,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         f4 lam0 = z4, lam1 = z4;
         h8 m0 = {}, m1h = {}, m1l = {};
         auto take_lam_m = [&](int c) {
-            const float *vh = sQV[c & 1] + KH_HALF_FLOATS;
+            const float *vh = sVH[c & 1];
             lam0 = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
             lam1 = *reinterpret_cast<const f4 *>(vh + VH_LAM + 16 + 4 * kk);
             const _Float16 *mp = reinterpret_cast<const _Float16 *>(vh + VH_MP);
@@ -938,23 +934,41 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     // barrier of step c).  The partial R = Q S^T of chunk c is formed at the
     // start of step c + 1, its products beside the split of the updated
     // state, from the split of the state before the update (kept) and Q of
-    // chunk c (read during step c); it reaches LDS before the barrier of step
-    // c + 1, where the output wave takes it.  Neither is on the path from the
-    // barrier of one step to that of the next.
+    // chunk c; it reaches LDS before the barrier of step c + 1, where the
+    // output wave takes it.  Q does not pass through LDS: each compute wave
+    // loads its Q operands of chunk c + 1 from the key-head slot in global
+    // memory (an L2 hit: twelve blocks share a slot) just before the barrier
+    // of step c, where no product is in flight, into the register set of
+    // chunk c - 1, whose R has been formed; sets alternate by chunk parity.
     lds_barrier();  // chunk 0's operands and chunk 1's K are in LDS
     h8 kph[2][2], kpl[2][2];
     key_ops(sKP[0], kpos(lane), kph, kpl);
-    // Q of the previous chunk; zero before chunk 0, whose step stores a zero
-    // R into the exchange slot of chunk -1 (the slot of chunk 1, rewritten
-    // before anything reads it)
-    h8 qph[2][2], qpl[2][2];
+    const _Float16 *qslot0 = reinterpret_cast<const _Float16 *>(p.ws + (int64_t)j * SCAN_KH_FLOATS) + KH_QP;
+    // this wave's Q operands of chunk cq (the positions they have in the slot)
+    auto q_load = [&](int cq, h8 (&qh)[2][2], h8 (&ql)[2][2]) {
+        const _Float16 *qb = qslot0 + chunk_slot(cu0, n, cq) * hk * (int64_t)(2 * SCAN_KH_FLOATS);
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int s = 2 * kh + i;
+                qh[tau][i] = *reinterpret_cast<const h8 *>(qb + kp_off(tau, s, 0) + lane * 8);
+                ql[tau][i] = *reinterpret_cast<const h8 *>(qb + kp_off(tau, s, 1) + lane * 8);
+            }
+    };
+    // chunk 0's Q in set A; set B holds zeros for the R of "chunk -1" that
+    // step 0 stores into the exchange slot of chunk 1 (rewritten before
+    // anything reads it)
+    h8 qphA[2][2], qplA[2][2], qphB[2][2], qplB[2][2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) qph[tau][i] = qpl[tau][i] = h8{};
+        for (int i = 0; i < 2; ++i) qphB[tau][i] = qplB[tau][i] = h8{};
+    q_load(0, qphA, qplA);
     // partial R = Q S^T (x256) of chunk cr from the split (shp, slp) of the
     // state before its update
-    auto r_partial = [&](int cr, const h8 (&shp)[2], const h8 (&slp)[2]) {
+    auto r_partial = [&](int cr, const h8 (&shp)[2], const h8 (&slp)[2], const h8 (&qph)[2][2],
+                         const h8 (&qpl)[2][2]) {
         const int xr = cr & 1;
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
@@ -971,11 +985,11 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     int kb_cur = 0;  // ring slot of this chunk's K (c % 3)
     // one chunk step: (sh, sl) receive the split of this chunk's state,
     // (shp, slp) hold the previous chunk's
-    auto step = [&](int c, h8 (&sh)[2], h8 (&sl)[2], const h8 (&shp)[2], const h8 (&slp)[2]) {
+    auto step = [&](int c, h8 (&sh)[2], h8 (&sl)[2], const h8 (&shp)[2], const h8 (&slp)[2],
+                    h8 (&qph)[2][2], h8 (&qpl)[2][2]) {
         const int x = c & 1;
         const int kb_next = kb_cur == 2 ? 0 : kb_cur + 1;
-        const float *qv = sQV[x];
-        const float *vh = qv + KH_HALF_FLOATS;
+        const float *vh = sVH[x];
         // partial P = K S^T (x256) over this wave's 64 keys, per token tile
 #pragma unroll
         for (int i = 0; i < 2; ++i) split8<true>(S4[2 * i], S4[2 * i + 1], sh[i], sl[i], d.ms);
@@ -992,7 +1006,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
                 for (int tau = 0; tau < 2; ++tau) kt[b][hl][tau] = kt_half(sKP[kb_cur], b, hl, tau);
         __builtin_amdgcn_sched_barrier(0);
         // the previous chunk's partial R
-        r_partial(c - 1, shp, slp);
+        r_partial(c - 1, shp, slp, qph, qpl);
         f4 Pp[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
@@ -1006,6 +1020,11 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
             Pp[tau] = (Phh + Plh) + Phl * LO_UNSCALE;
             sXP[x][wave][tau][lane] = Pp[tau];
         }
+        // chunk c + 1's Q into the set R of chunk c - 1 has just used (the
+        // products' results are stored, so none is in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < n_chunks) q_load(c + 1, qph, qpl);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();  // partials visible; every wave is past chunk c - 1
         __builtin_amdgcn_sched_barrier(0);  // nothing below moves up before the barrier
 
@@ -1070,7 +1089,6 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         // (here no product of this step is in flight: a load issued while one
         // is may be given the registers of its operands, see tests/asm_hazards.py)
         __builtin_amdgcn_sched_barrier(0);
-        key_ops(qv, lane, qph, qpl);
         if (c + 1 < n_chunks) key_ops(sKP[kb_next], kpos(lane), kph, kpl);
         __builtin_amdgcn_sched_barrier(0);
         // 16 S' = Lam_last (16 S) + (16 K)^T (D[last] U) over the 32 permuted
@@ -1090,14 +1108,14 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     h8 shA[2] = {}, slA[2] = {}, shB[2] = {}, slB[2] = {};
     int c = 0;
     for (; c + 1 < n_chunks; c += 2) {
-        step(c, shA, slA, shB, slB);
-        step(c + 1, shB, slB, shA, slA);
+        step(c, shA, slA, shB, slB, qphB, qplB);
+        step(c + 1, shB, slB, shA, slA, qphA, qplA);
     }
     if (c < n_chunks) {
-        step(c, shA, slA, shB, slB);
-        r_partial(c, shA, slA);
+        step(c, shA, slA, shB, slB, qphB, qplB);
+        r_partial(c, shA, slA, qphA, qplA);
     } else {
-        r_partial(c - 1, shB, slB);
+        r_partial(c - 1, shB, slB, qphB, qplB);
     }
     lds_barrier();  // R and U of the last chunk are visible to the output wave
 #pragma unroll
