@@ -1273,6 +1273,7 @@ __global__ __launch_bounds__(256) void layer_prep_kernel(LayerPrepArgs p, PrepDi
 // head j for four of the chunk's tokens, with all its loads issued up front.
 // Same per-element arithmetic as gdn_pre, so the results equal the staged
 // path's bit for bit.
+static_assert(LAYER_G_MAX * CT <= CHUNK_PREP_THREADS, "one gate pair per thread");
 __global__ __launch_bounds__(256) void layer_prep_f16_kernel(LayerPrepArgs p, PrepDims d)
 {
     __shared__ __attribute__((aligned(16))) PrepShared sm;
@@ -1304,6 +1305,20 @@ __global__ __launch_bounds__(256) void layer_prep_f16_kernel(LayerPrepArgs p, Pr
     // the seven X rows of the task's four tokens; rows past the chunk's end
     // repeat its last row (valid memory, results unused)
     Raw8<_Float16> wr[4], xa[7];
+    // the gate inputs of pair tid = (value head gh of the group, token t),
+    // requested with the rows so that their latency overlaps them (pairs
+    // past the chunk's end, and threads past G * CT, load nothing)
+    const int gh_t = tid / CT, gt_t = tid - gh_t * CT;
+    const bool gate_t = tid < G * CT, gate_ld = gate_t && gt_t < nv;
+    _Float16 ga = 0, gdt = 0, gal = 0, gb = 0;
+    if (gate_ld) {
+        const int h = j * G + gh_t;
+        const int64_t e = ((int64_t)cu0 + c * CT + gt_t) * hv + h;
+        ga = static_cast<const _Float16 *>(p.a)[e];
+        gb = static_cast<const _Float16 *>(p.b)[e];
+        gdt = static_cast<const _Float16 *>(p.dt_bias)[h];
+        gal = static_cast<const _Float16 *>(p.A_log)[h];
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) wr[k].load(cw + (int64_t)(ch + 64 * (k >> 1)) * 4 + (k & 1) * 8);
 #pragma unroll
@@ -1334,19 +1349,11 @@ __global__ __launch_bounds__(256) void layer_prep_f16_kernel(LayerPrepArgs p, Pr
 
     // gates of the group's value heads, token t of head gh at sGate[gh][.][t]
     // (zero past the end)
-    if (wave == CHUNK_PREP_THREADS / 64 - 1) {
-        for (int i = lane; i < G * CT; i += 64) {
-            const int gh = i / CT, t = i - gh * CT, h = j * G + gh;
-            float g = 0.f, bt = 0.f;
-            if (t < nv) {
-                const int64_t e = ((int64_t)cu0 + c * CT + t) * hv + h;
-                gates(ld1(static_cast<const _Float16 *>(p.a) + e), ld1(static_cast<const _Float16 *>(p.dt_bias) + h),
-                      ld1(static_cast<const _Float16 *>(p.A_log) + h), ld1(static_cast<const _Float16 *>(p.b) + e),
-                      g, bt);
-            }
-            sGate[gh][0][t] = g;
-            sGate[gh][1][t] = bt;
-        }
+    if (gate_t) {
+        float g = 0.f, bt = 0.f;
+        if (gate_ld) gates((float)ga, (float)gdt, (float)gal, (float)gb, g, bt);
+        sGate[gh_t][0][gt_t] = g;
+        sGate[gh_t][1][gt_t] = bt;
     }
     __syncthreads();
 
