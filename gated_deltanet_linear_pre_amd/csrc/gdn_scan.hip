@@ -62,10 +62,11 @@
 //   recurrence.  Every product consumes the layout the previous one produced,
 //   so the state never leaves registers.
 //   A copy wave moves the chunk operands from global memory into LDS a step
-//   ahead (K two steps ahead: the compute waves read it one step early).  An
-//   output wave forms O = Lam R + M U one step behind, from the partial
-//   Q S^T and U the compute waves leave in LDS, so the outputs stay off the
-//   recurrence's path.  In the layer path with fp16 inputs a v wave forms v
+//   ahead (K two steps ahead: the compute waves read it one step early); Q
+//   goes from the workspace straight into the compute waves' registers.  Two
+//   output waves (one per row group) form O = Lam R + M U one step behind,
+//   from the partial Q S^T and U the compute waves leave in LDS, so the
+//   outputs stay off the recurrence's path.  In the layer path with fp16 inputs a v wave forms v
 //   of the block's channels from the raw qkv rows the copy wave brings (conv
 //   with the history, SiLU: the pre stage's expressions) and carries their
 //   history, so the fp32 v never goes through memory.
