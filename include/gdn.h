@@ -251,7 +251,7 @@ int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w,
  *
  * Shapes whose gdn_prefill_workspace_bytes exceeds GDN_NOALLOC_SCRATCH_BYTES
  * are rejected with GDN_E_TOO_LARGE before anything is enqueued (at
- * production width, 16 key and 48 value heads, about 2300 tokens fit).  The
+ * production width, 16 key and 48 value heads, about 2600 tokens fit).  The
  * array's device address is looked up on the first call on each device
  * (GDN_E_LAUNCH if the runtime refuses).  Every call on one GPU shares that
  * GPU's array: calls that overlap in time on one GPU (on different streams,
