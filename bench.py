@@ -367,6 +367,16 @@ def main():
             for d in ls:
                 B.gdn_step(shape, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"],
                            d["z"], d["gamma"], d["hist"], d["S0"], y)
+
+        # the history alternating between two buffers per layer: one launch
+        # per layer and step (two steps per call, back to the first buffer)
+        hists = [[d["hist"], torch.empty_like(d["hist"])] for d in ls]
+
+        def two_alt():
+            for s_ in range(2):
+                for d, hs in zip(ls, hists):
+                    B.gdn_step(shape, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                               d["z"], d["gamma"], hs[s_], d["S0"], y, hist_out=hs[1 - s_])
         def timed(fn):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -388,6 +398,14 @@ def main():
             one()
         graph.replay()
         us_g = timed(graph.replay)
+        for _ in range(2):
+            two_alt()
+        us_a = timed(two_alt) / 2
+        graph_a = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_a):
+            two_alt()
+        graph_a.replay()
+        us_ag = timed(graph_a.replay) / 2
         C = 2 * hk * 128 + hv * 128
         byts = batch * (2 * hv * 128 * 128 * 4 + C * 2 + 4 * 3 * C * 2 + 2 * hv * 2 + 2 * hv * 128 * 2)
         return {"batch": batch, "us_per_layer": round(us, 2),
@@ -395,7 +413,10 @@ def main():
                 "us_per_layer_graph": round(us_g, 2),
                 "tokens_per_s_graph": round(batch / (us_g * 1e-6 * layers), 1),
                 "bytes_per_layer": byts, "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "hbm_frac_graph": round(byts / (us_g * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                "hbm_frac_graph": round(byts / (us_g * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "us_per_layer_alternating": round(us_a, 2),
+                "us_per_layer_alternating_graph": round(us_ag, 2),
+                "tokens_per_s_alternating_graph": round(batch / (us_ag * 1e-6 * layers), 1)}
 
     def varlen(steps, warmup):
         # the long varlen batch through gdn_prefill_layer, 36 layers in order,

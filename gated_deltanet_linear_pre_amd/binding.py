@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill_layer_noalloc.restype = I
         L.gdn_prefill_layer_noalloc.argtypes = [SP] + [P] * 13
         L.gdn_step.restype = I
-        L.gdn_step.argtypes = [SP] + [P] * 12
+        L.gdn_step.argtypes = [SP] + [P] * 13
         _lib = L
     return _lib
 
@@ -178,9 +178,9 @@ def gdn_prefill_layer_noalloc(shape, cu_seqlens, qkv, conv_w, a, b, A_log, dt_bi
 
 
 def gdn_step(shape, qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist, state, y, stream=None,
-             check=True) -> int:
+             check=True, hist_out=None) -> int:
     st = lib().gdn_step(ctypes.byref(shape), *map(_ptr, (qkv, conv_w, a, b, A_log, dt_bias, z,
-                                                            gamma, hist, state, y)),
+                                                            gamma, hist, hist_out, state, y)),
                         _stream(stream))
     if check:
         _check("gdn_step", st)

@@ -265,7 +265,7 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
 
 int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w, const void *a,
              const void *b, const void *A_log, const void *dt_bias, const void *z,
-             const void *gamma, void *hist, float *state, void *y, void *stream)
+             const void *gamma, void *hist, void *hist_out, float *state, void *y, void *stream)
 {
     int st = check_shape(shape);
     if (st) return st;
@@ -275,7 +275,9 @@ int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w, const 
     ALN(a, 4); ALN(b, 4); ALN(A_log, 4); ALN(dt_bias, 4);
     ALN(qkv, 16); ALN(conv_w, 16); ALN(z, 16); ALN(gamma, 16); ALN(hist, 16); ALN(state, 16);
     ALN(y, 16);
-    const StepArgs sa{qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist, state, y};
+    if (hist_out == hist) hist_out = nullptr;  // in place
+    if (hist_out) ALN(hist_out, 16);
+    const StepArgs sa{qkv, conv_w, a, b, A_log, dt_bias, z, gamma, hist, hist_out, state, y};
     return launch_status(gdn::launch_step(*shape, sa, (hipStream_t)stream));
 }
 

@@ -59,6 +59,7 @@ struct PostArgs {
 struct StepArgs {
     const void *qkv, *conv_w, *a, *b, *A_log, *dt_bias, *z, *gamma;
     void *hist;
+    void *hist_out;  // NULL: hist is shifted in place by a second launch
     float *state;
     void *y;
 };

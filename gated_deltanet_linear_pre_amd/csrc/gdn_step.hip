@@ -35,8 +35,13 @@
 //     o = alpha (S q^) + u (k^.q^) is the same quantity as (alpha S + u k^T) q^
 //     in one pass;
 //   - the RMSNorm over the head's 128 outputs and the gated output.
-// A second launch shifts the history (every block of a key-head group reads
-// the group's q/k history, so no block of the first launch may overwrite it).
+// With the new history going to its own buffer (hist_out), the step kernel
+// writes it too: each block the rows of its value head's v channels, the
+// first block of each key-head group those of the group's q and k channels,
+// all read from the old history, which no block writes: one launch.  In
+// place, a second launch shifts the history (every block of a key-head group
+// reads the group's q/k history, so no block of the first launch may
+// overwrite it).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -124,6 +129,20 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs p, StepDims d)
     const float q = cv4(wq, xq);
     const float k = cv4(wk, xk);
     const float v = cv4(wv, xv);
+    // the new history X[1..3] of this block's channels, when it has a
+    // buffer of its own
+    if (p.hist_out && tid < 128) {
+        TI *ho = static_cast<TI *>(p.hist_out) + (int64_t)n * 3 * C;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) ho[m * C + chv] = xv[m + 1];
+        if (h % d.G == 0) {
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                ho[m * C + chq] = xq[m + 1];
+                ho[m * C + chk] = xk[m + 1];
+            }
+        }
+    }
     float sumq = 0.f, sumk = 0.f, sumqk = 0.f;
     if (tid < 128) {
         sq[c] = q;
@@ -248,7 +267,7 @@ static hipError_t launch_step_t(const gdn_shape &s, const StepArgs &a, hipStream
     hipLaunchKernelGGL((step_kernel<TI, TO>), dim3((unsigned)(s.n_seq * (int64_t)s.hv)), dim3(256),
                        0, st, a, d);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.hist_out) return e;
     const int64_t threads = (int64_t)s.n_seq * (d.C / 8);
     hipLaunchKernelGGL((step_hist_kernel<TI>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        st, static_cast<const TI *>(a.qkv), static_cast<TI *>(a.hist), d.C, s.n_seq);

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -229,16 +229,22 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens,
  *   alpha = exp(g), g and beta as in gdn_pre;
  *   S <- alpha*S + beta (v - alpha*S kn) kn^T,  o = S qn / sqrt(dk)  (fp32)
  *   y = o / sqrt(mean(o^2) + eps_rms) * gamma * z * sigmoid(z)  -> out_dtype
- *   hist[n] <- X[1..3]
+ *   hist_out[n] <- X[1..3]
  * In:  qkv [n_seq][C], conv_w, a, b [n_seq][hv], A_log, dt_bias, z
  *      [n_seq][hv][dv], gamma; hist and state (read).
- * Out: y [n_seq][hv][dv]; hist and state (overwritten in place).
- * No workspace.  Two kernels are enqueued (the step, then the history shift).
+ * Out: y [n_seq][hv][dv]; state (overwritten in place); the new history in
+ *      hist_out, a buffer of hist's layout and dtype that must not overlap
+ *      hist (16-byte aligned), which stays unchanged; or, with hist_out NULL
+ *      or equal to hist, in hist itself.
+ * No workspace.  One kernel is enqueued with a separate hist_out; in place,
+ * two (the step, then the history shift, since every block of a key-head
+ * group reads the group's old history).  A decode loop that alternates two
+ * history buffers gets the single launch.
  */
 int gdn_step(const gdn_shape *shape, const void *qkv, const void *conv_w,
              const void *a, const void *b, const void *A_log,
              const void *dt_bias, const void *z, const void *gamma, void *hist,
-             float *state, void *y, void *stream);
+             void *hist_out, float *state, void *y, void *stream);
 
 /*
  * gdn_prefill_layer_noalloc -- for callers that cannot allocate device memory

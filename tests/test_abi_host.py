@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert B.gdn_abi_version() == 4
+    assert B.gdn_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert B.gdn_status_str(code) and B.gdn_status_str(code) != "unknown status"
     assert B.gdn_status_str(-99) == "unknown status"
@@ -201,6 +201,13 @@ def test_step_shape_rules():
 def test_step_null_and_alignment(name):
     assert _step(step_shape(), **{name: None}) == -1
     assert _step(step_shape(), **{name: P + 2}) == -3
+
+
+def test_step_hist_out_alignment():
+    # a separate history output is optional, but aligned like hist when given
+    s = step_shape()
+    args = dict(qkv=P, conv_w=P, a=P, b=P, A_log=P, dt_bias=P, z=P, gamma=P, hist=P, state=P, y=P)
+    assert B.gdn_step(s, *args.values(), stream=0, check=False, hist_out=P + 8) == -3
 
 
 

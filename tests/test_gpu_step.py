@@ -150,3 +150,100 @@ def test_step_graph_replay_matches_eager(gpu):
             assert np.array_equal(np_(b.y).view(np.uint16), y.view(np.uint16)), f"y, replay {rep}"
             assert np.array_equal(np_(b.state).view(np.uint32), s.view(np.uint32)), f"state, replay {rep}"
             assert np.array_equal(np_(b.hist).view(np.uint16), h.view(np.uint16)), f"hist, replay {rep}"
+
+
+
+def _step_out(buf, hist_in, hist_out, y=None, state=None, qkv=None):
+    B.gdn_step(buf.shape, buf.qkv if qkv is None else qkv, buf.conv_w, buf.a, buf.b, buf.A_log,
+               buf.dt_bias, buf.z, buf.gamma, hist_in, buf.state if state is None else state,
+               buf.y if y is None else y, hist_out=hist_out)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[4], CASES[5]], ids=lambda c: c[0])
+def test_step_hist_out_matches_in_place(gpu, case):
+    # the new history written to a buffer of its own (one launch) gives the
+    # in-place call's y, state and history bit for bit, and leaves the input
+    # history untouched
+    name, hk, hv, n, io, out = case
+    w = synth.Workload(name, hk=hk, hv=hv, seqlens=(1,) * n, io=io, out=out, seed=(35, n),
+                       s0_std=0.05, hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    a = LayerBuffers.create(w, inp)
+    b = LayerBuffers.create(w, inp)
+    banner("gdn_step", name, "in place")
+    _step(a)
+    hist0 = b.hist.clone()
+    y = Guarded(tuple(b.y.shape), b.y.dtype)
+    state = Guarded(tuple(b.state.shape), torch.float32, init=b.state)
+    hist_out = Guarded(tuple(b.hist.shape), b.hist.dtype)
+    banner("gdn_step", name, "hist_out")
+    _step_out(b, b.hist, hist_out.t, y=y.t, state=state.t)
+    torch.cuda.synchronize()
+    assert y.intact() and state.intact() and hist_out.intact()
+    bits = np.uint16 if io == "f16" else np.uint32
+    ybits = np.uint16 if out == "f16" else np.uint32
+    assert np.array_equal(np_(y.t).view(ybits), np_(a.y).view(ybits))
+    assert np.array_equal(np_(state.t).view(np.uint32), np_(a.state).view(np.uint32))
+    assert np.array_equal(np_(hist_out.t).view(bits), np_(a.hist).view(bits))
+    assert np.array_equal(np_(b.hist).view(bits), np_(hist0).view(bits))
+
+
+def test_steps_alternating_history_match_in_place(gpu):
+    # 9 decode steps over 3 layers with each layer's history alternating
+    # between two buffers (one launch per step and layer) equal the in-place
+    # steps bit for bit, run eagerly and replayed from a HIP graph of two
+    # steps (the graph reads the token rows from fixed staging buffers that
+    # are refilled between replays)
+    L, T, n = 3, 9, 4
+    w = synth.Workload("step_alternating", hk=16, hv=48, seqlens=(1,) * n, seed=(36,),
+                       s0_std=0.05, hist_std=1.0)
+    inps = [synth.layer_inputs(w, l) for l in range(L)]
+    rng = np.random.default_rng(36)
+    toks = [[torch.from_numpy(rng.standard_normal(inps[l]["qkv"].shape).astype(np.float16)).cuda()
+             for l in range(L)] for _ in range(T)]
+    ref = [LayerBuffers.create(w, inp) for inp in inps]
+    banner("gdn_step", w.name, "in place")
+    for t in range(T):
+        for l, b in enumerate(ref):
+            _step_out(b, b.hist, None, qkv=toks[t][l])
+    torch.cuda.synchronize()
+
+    def check(bufs, hs, mode):
+        for l, b in enumerate(bufs):
+            assert np.array_equal(np_(b.y).view(np.uint16), np_(ref[l].y).view(np.uint16)), mode
+            assert np.array_equal(np_(b.state).view(np.uint32), np_(ref[l].state).view(np.uint32)), mode
+            assert np.array_equal(np_(hs[l][T % 2]).view(np.uint16), np_(ref[l].hist).view(np.uint16)), mode
+
+    def fresh():
+        bufs = [LayerBuffers.create(w, inp) for inp in inps]
+        return bufs, [[b.hist, torch.empty_like(b.hist)] for b in bufs]
+
+    banner("gdn_step", w.name, "alternating, eager")
+    bufs, hs = fresh()
+    for t in range(T):
+        for l, b in enumerate(bufs):
+            _step_out(b, hs[l][t % 2], hs[l][1 - t % 2], qkv=toks[t][l])
+    torch.cuda.synchronize()
+    check(bufs, hs, "eager")
+
+    banner("gdn_step", w.name, "alternating, graph of two steps")
+    bufs, hs = fresh()
+    stage = [[torch.empty_like(toks[0][l]) for l in range(L)] for _ in range(2)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(2):
+            for l, b in enumerate(bufs):
+                _step_out(b, hs[l][s], hs[l][1 - s], qkv=stage[s][l])
+    torch.cuda.synchronize()
+    for t in range(0, T - 1, 2):
+        for s in range(2):
+            for l in range(L):
+                stage[s][l].copy_(toks[t + s][l])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+    for l, b in enumerate(bufs):  # the odd last step, eagerly
+        _step_out(b, hs[l][(T - 1) % 2], hs[l][T % 2], qkv=toks[T - 1][l])
+    torch.cuda.synchronize()
+    check(bufs, hs, "graph")
