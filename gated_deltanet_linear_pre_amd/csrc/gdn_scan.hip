@@ -904,8 +904,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 #pragma unroll
     for (int b = 0; b < 4; ++b) S4[b] = *reinterpret_cast<const f4 *>(Srow + 16 * b) * KQ_SCALE;
 
-    // this wave's two 32-key steps of K (pos = kpos(lane)) or Q (pos = lane)
-    // of both token tiles, hi and lo
+    // this wave's two 32-key steps of K of both token tiles, hi and lo (at
+    // positions pos = kpos(lane))
     auto key_ops = [&](const float *base, int pos, h8 (&hi)[2][2], h8 (&lo)[2][2]) {
         const _Float16 *kb = reinterpret_cast<const _Float16 *>(base);
 #pragma unroll
@@ -935,8 +935,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     // barrier of step c).  The partial R = Q S^T of chunk c is formed at the
     // start of step c + 1, its products beside the split of the updated
     // state, from the split of the state before the update (kept) and Q of
-    // chunk c; it reaches LDS before the barrier of step c + 1, where the
-    // output wave takes it.  Q does not pass through LDS: each compute wave
+    // chunk c; it reaches LDS before the barrier of step c + 1, after which
+    // the output waves take it.  Q does not pass through LDS: each compute wave
     // loads its Q operands of chunk c + 1 from the key-head slot in global
     // memory (an L2 hit: twelve blocks share a slot) just before the barrier
     // of step c, where no product is in flight, into the register set of
@@ -1032,7 +1032,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         // Reads in the order they are needed, since each wave's LDS reads
         // complete in order and four waves read at once after the barrier:
         // what B needs (the partner's partial P, Lam, beta, v); then T and
-        // the last-row decays; Q and the next chunk's K once U is formed.
+        // the last-row decays; the next chunk's K once U is formed.
         const f4 Po0 = sXP[x][partner][0][lane];
         const f4 Po1 = sXP[x][partner][1][lane];
         const f4 lam0 = *reinterpret_cast<const f4 *>(vh + VH_LAM + 4 * kk);
