@@ -466,14 +466,22 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             // the first product's accumulator layout (W[4 kk + r][l16] in
             // component r) is the second's B operand as it stands:
             //   W = A10 T00,  T10 = -(T11 W)
+            // (every operand read before the first product: a read issued while
+            // a product is in flight may be given the registers of its operands)
+            float wa[4], wb[4], ta[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wa[i] = sA[16 + l16][4 * kk + i];
+                wb[i] = sT[4 * kk + i][l16];
+                ta[i] = sT[16 + l16][16 + 4 * kk + i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f4 W = z4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                W = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 + l16][4 * kk + i], sT[4 * kk + i][l16], W, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) W = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[i], wb[i], W, 0, 0, 0);
             f4 T10 = z4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[16 + l16][16 + 4 * kk + i], W[i], T10, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(ta[i], W[i], T10, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sT[16 + 4 * kk + r][l16] = -T10[r];
         }
@@ -973,14 +981,16 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         const int xr = cr & 1;
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            f4 Rhh = z4, Rhl = z4, Rlh = z4;
+            // the two unscaled terms share one chain, the scaled one has its own
+            f4 Rh = z4, Rl = z4;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                Rhh = mfma_k32(qph[tau][i], shp[i], Rhh);
-                Rhl = mfma_k32(qph[tau][i], slp[i], Rhl);   // x LO_SCALE
-                Rlh = mfma_k32(qpl[tau][i], shp[i], Rlh);
+                Rh = mfma_k32(qph[tau][i], shp[i], Rh);
+                Rl = mfma_k32(qph[tau][i], slp[i], Rl);   // x LO_SCALE
             }
-            sXR[xr][wave][tau][lane] = (Rhh + Rlh) + Rhl * LO_UNSCALE;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) Rh = mfma_k32(qpl[tau][i], shp[i], Rh);
+            sXR[xr][wave][tau][lane] = Rh + Rl * LO_UNSCALE;
         }
     };
     int kb_cur = 0;  // ring slot of this chunk's K (c % 3)
@@ -1011,14 +1021,15 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         f4 Pp[2];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            f4 Phh = z4, Phl = z4, Plh = z4;
+            f4 Ph = z4, Pl = z4;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                Phh = mfma_k32(kph[tau][i], sh[i], Phh);
-                Phl = mfma_k32(kph[tau][i], sl[i], Phl);   // x LO_SCALE
-                Plh = mfma_k32(kpl[tau][i], sh[i], Plh);
+                Ph = mfma_k32(kph[tau][i], sh[i], Ph);
+                Pl = mfma_k32(kph[tau][i], sl[i], Pl);   // x LO_SCALE
             }
-            Pp[tau] = (Phh + Plh) + Phl * LO_UNSCALE;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) Ph = mfma_k32(kpl[tau][i], sh[i], Ph);
+            Pp[tau] = Ph + Pl * LO_UNSCALE;
             sXP[x][wave][tau][lane] = Pp[tau];
         }
         // chunk c + 1's Q into the set R of chunk c - 1 has just used (the
