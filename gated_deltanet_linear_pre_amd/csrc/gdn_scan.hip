@@ -633,8 +633,6 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     __shared__ __attribute__((aligned(16))) f4 sXP[2][CHUNK_WAVES][2][64];
     __shared__ __attribute__((aligned(16))) f4 sXR[2][CHUNK_WAVES][2][64];
     __shared__ __attribute__((aligned(16))) f4 sU[2][CHUNK_WAVES / 2][2][64];
-    // each output wave's tile of o (32 tokens x its 16 channels), rows padded
-    __shared__ __attribute__((aligned(16))) float sO[2][CT][20];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -755,8 +753,7 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
         // compute waves through LDS: written after the barrier of step c,
         // overwritten (for chunk c + 2) only after that of step c + 2.  Lam and
         // M are read from chunk c's value-head slot during step c (before the
-        // copy of chunk c + 2 may replace it) and kept in registers.  The tile
-        // goes out through LDS as whole 64-byte row pieces.
+        // copy of chunk c + 2 may replace it) and kept in registers.
         const int g = wave - OUT_WAVE;
         f4 lam0 = z4, lam1 = z4;
         h8 m0 = {}, m1h = {}, m1l = {};
@@ -789,30 +786,23 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
             f4 O1 = mfma_k32(m1h, cat(uh0, uh1), lam1 * R1);
             O1 = mfma_k32(m1l, cat(uh0, uh1), O1);
             O1 = mfma_k32(m1hs, cat(ul0, ul1), O1) * SCALE;
+            // straight from the accumulators: lane (l16, kk) writes channel l16
+            // of tokens 4 kk + r and 16 + 4 kk + r (each store instruction
+            // covers 64 contiguous bytes of four token rows)
+            float *ob = p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + g * 16 + l16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sO[g][4 * kk + r][l16] = O0[r];
-                sO[g][16 + 4 * kk + r][l16] = O1[r];
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // lane l takes token 16 m + l / 4, channels 4 (l % 4) .. + 3 of the
-            // group's 16
-            float *ob = p.o + (tb * hv + h) * 128 + rb * CHUNK_ROWS + g * 16 + (lane & 3) * 4;
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int t = 16 * m + (lane >> 2);
-                const f4 v = *reinterpret_cast<const f4 *>(&sO[g][t][(lane & 3) * 4]);
-                if (t < nv) *reinterpret_cast<f4 *>(ob + (uint32_t)t * vstride) = v;
+                const int t0 = 4 * kk + r, t1 = 16 + 4 * kk + r;
+                if (t0 < nv) ob[(uint32_t)t0 * vstride] = O0[r];
+                if (t1 < nv) ob[(uint32_t)t1 * vstride] = O1[r];
             }
         };
         side_barrier();
         for (int c = 0; c < n_chunks; ++c) {
             side_barrier();
             // let the compute waves' reads that the recurrence waits for
-            // reach the LDS first (~512 cycles)
-            __builtin_amdgcn_s_sleep(8);
+            // reach the LDS first (~256 cycles)
+            __builtin_amdgcn_s_sleep(4);
             if (c > 0) o_store(c - 1);
             take_lam_m(c);
         }
