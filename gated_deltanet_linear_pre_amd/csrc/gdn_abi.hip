@@ -107,7 +107,7 @@ namespace {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Carve {
-    size_t qn, kn, vc, g, beta, o, scan, total;
+    size_t qn, kn, vc, g, beta, o, scan, sync, total;
 };
 
 // Which path gdn_prefill_layer takes for a shape: the pre stage fused into the
@@ -123,7 +123,8 @@ LayerPath layer_path(const gdn_shape *s)
 
 // The layer workspace holds what the path writes and reads back: o and the
 // scan scratch always; the fp32 v when the fused prep forms it (fp32 inputs);
-// q, k, v and the gates only on the staged path.
+// q, k, v and the gates only on the staged path; with fp16 inputs the
+// counters of post run in the chunk kernel's launch.
 Carve carve(const gdn_shape *s)
 {
     const size_t T = (size_t)s->total_T;
@@ -138,6 +139,7 @@ Carve carve(const gdn_shape *s)
     c.beta = off; off += staged ? round256(T * s->hv * sizeof(float)) : 0;
     c.o = off; off += round256(T * s->hv * 128 * sizeof(float));
     c.scan = off; off += round256(gdn::scan_workspace_bytes(*s));
+    c.sync = off; off += path == LayerPath::fused_f16 ? round256(gdn::layer_sync_bytes(*s)) : 0;
     c.total = off;
     return c;
 }
@@ -250,16 +252,20 @@ int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens, const v
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
     const ScanArgs sa{cu_seqlens, qn, kn, vc, g, beta, state, o, sws};
-    if (layer_path(shape) != LayerPath::staged) {
+    const PostArgs po{o, z, gamma, y};
+    const LayerPath path = layer_path(shape);
+    if (path != LayerPath::staged) {
         // pre fused into the scan's prep step: q, k and the gates stay on chip
-        const gdn::LayerPrepArgs lp{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, vc, sws};
-        if (gdn::launch_layer_scan(*shape, lp, sa, s) != hipSuccess) return GDN_E_LAUNCH;
+        uint32_t *sync = path == LayerPath::fused_f16 ? reinterpret_cast<uint32_t *>(ws + c.sync) : nullptr;
+        const gdn::LayerPrepArgs lp{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, vc, sws, sync};
+        bool post_done = false;
+        if (gdn::launch_layer_scan(*shape, lp, sa, &po, &post_done, s) != hipSuccess) return GDN_E_LAUNCH;
+        if (post_done) return GDN_OK;
     } else {
         const PreArgs pa{cu_seqlens, qkv, conv_w, a, b, A_log, dt_bias, hist, qn, kn, vc, g, beta};
         if (gdn::launch_pre(*shape, pa, s) != hipSuccess) return GDN_E_LAUNCH;
         if (gdn::launch_scan(*shape, sa, s) != hipSuccess) return GDN_E_LAUNCH;
     }
-    const PostArgs po{o, z, gamma, y};
     return launch_status(gdn::launch_post(*shape, po, s));
 }
 

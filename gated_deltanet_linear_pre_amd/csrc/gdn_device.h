@@ -57,6 +57,22 @@ __device__ __forceinline__ float silu_fast(float x)
 // 1 / sqrt(x) on v_rsq_f32 (1 ulp).
 __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// ---- the post stage's arithmetic on one row, shared by every kernel that
+// runs it (so that their results agree bit for bit): a 16-lane DPP row holds
+// 128 values, 8 per lane; y = ((x inv) gamma) silu(z), inv = 1 / sqrt(mean(x^2)
+// + eps), the sum of squares in lane order then across the row.
+__device__ __forceinline__ void post_row(const float (&x)[8], const float (&zz)[8],
+                                         const float (&gm)[8], float eps, float (&out)[8])
+{
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+    ss = row_sum16(ss);
+    const float inv = rsqrt_fast(ss * (1.0f / 128.0f) + eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = ((x[i] * inv) * gm[i]) * silu_fast(zz[i]);
+}
+
 // ---- per-element arithmetic of the pre stage, shared by every kernel that
 // runs it (one expression, so the compiler rounds it the same way everywhere)
 // 4-tap conv of one channel: taps in order, tap 3 on the current token.  The

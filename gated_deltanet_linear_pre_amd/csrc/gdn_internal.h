@@ -47,7 +47,11 @@ struct LayerPrepArgs {
     void *hist;
     float *vc;
     float *ws;
+    // fp16 io: room (layer_sync_bytes) for the counters and status word of
+    // post run in the chunk kernel's launch (null: post is not fused)
+    uint32_t *sync;
 };
+size_t layer_sync_bytes(const gdn_shape &s);
 constexpr int LAYER_G_MAX = 8;  // value heads per key head the fused step handles
 
 struct PostArgs {
@@ -74,8 +78,10 @@ int check_layer_args(const int32_t *cu, const void *qkv, const void *conv_w, con
 
 hipError_t launch_pre(const gdn_shape &s, const PreArgs &a, hipStream_t st);
 hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st);
+// The layer's pre and scan; with post given, also post when it can run in the
+// chunk kernel's launch (then *post_done is set, else the caller launches it).
 hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const ScanArgs &a,
-                             hipStream_t st);
+                             const PostArgs *post, bool *post_done, hipStream_t st);
 hipError_t launch_post(const gdn_shape &s, const PostArgs &a, hipStream_t st);
 hipError_t launch_step(const gdn_shape &s, const StepArgs &a, hipStream_t st);
 

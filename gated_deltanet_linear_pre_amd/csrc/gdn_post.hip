@@ -35,18 +35,8 @@ __global__ __launch_bounds__(256) void post_kernel(const float *__restrict__ o,
     load8_split(z + base, zz);
     load8_split(gamma + l16 * 4, gm);
 
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
-    ss = row_sum16(ss);
-    const float inv = rsqrt_fast(ss * (1.0f / 128.0f) + eps);
-
     float out[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float gate = silu_fast(zz[i]);
-        out[i] = ((x[i] * inv) * gm[i]) * gate;
-    }
+    post_row(x, zz, gm, eps, out);
     store8_split(y + base, out);
 }
 

@@ -79,6 +79,9 @@
 // Determinism: fixed-order MFMA chains, no atomics.  Splitting a sequence at a
 // multiple of 32 tokens gives bit-identical results; other split points agree
 // within rounding (the chunk grid moves).
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -617,22 +620,52 @@ __device__ __forceinline__ void side_barrier()
 
 // LDS rings: chunk c's K in sKP[c % 3] (read a step ahead for K S^T, and as
 // K^T in step c); its value-head slot in sVH[c % 2]; with RAW_V its raw
-// fp16 v rows in sRaw[c % 3]; its fp32 v in sV[c % 2].
+// fp16 v rows in sRaw[c % 3]; its fp32 v in sV[c % 2].  Every member's size
+// is a multiple of 256 bytes but the last.
 template <bool RAW_V>
-__global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanArgs p, ChunkDims d,
-                                                                         VRawArgs vr)
-{
-    __shared__ __attribute__((aligned(16))) float sKP[3][KH_HALF_FLOATS];
-    __shared__ __attribute__((aligned(16))) float sVH[2][SCAN_SLOT_FLOATS];
-    constexpr int RAW_BUF = RAW_V ? 3 : 1;
-    __shared__ __attribute__((aligned(16))) _Float16 sRaw[RAW_BUF][CT][CHUNK_ROWS];
-    __shared__ __attribute__((aligned(16))) _Float16 sRawH[3][CHUNK_ROWS];
-    __shared__ __attribute__((aligned(16))) float sV[2][CT][CHUNK_ROWS];
+struct __attribute__((aligned(16))) ChunkShared {
+    float sKP[3][KH_HALF_FLOATS];
+    float sVH[2][SCAN_SLOT_FLOATS];
+    _Float16 sRaw[RAW_V ? 3 : 1][CT][CHUNK_ROWS];
+    float sV[2][CT][CHUNK_ROWS];
     // partial K S^T and Q S^T of every compute wave per token tile, and U of
     // each row group
-    __shared__ __attribute__((aligned(16))) f4 sXP[2][CHUNK_WAVES][2][64];
-    __shared__ __attribute__((aligned(16))) f4 sXR[2][CHUNK_WAVES][2][64];
-    __shared__ __attribute__((aligned(16))) f4 sU[2][CHUNK_WAVES / 2][2][64];
+    f4 sXP[2][CHUNK_WAVES][2][64];
+    f4 sXR[2][CHUNK_WAVES][2][64];
+    f4 sU[2][CHUNK_WAVES / 2][2][64];
+    _Float16 sRawH[3][CHUNK_ROWS];
+};
+
+// With SIGNAL (the layer step that runs post in the same launch, one
+// sequence), the output waves store o with device-scope stores and, once the
+// stores of chunk c have completed, add 1 to the counter of (c, h): the eight
+// output waves of value head h (four channel blocks, two row groups) take it
+// to 8, after which every value of o of chunk c and head h is visible to a
+// device-scope load anywhere on the device.  Each counter has a 256-byte line
+// of its own (COUNT_STRIDE words): packed, the post waves' polls of a few
+// lines slowed the whole chip (by ~30 us per layer).
+struct OutSignal {
+    uint32_t *count;
+};
+constexpr uint32_t O_WRITERS = 2 * (128 / CHUNK_ROWS);  // output waves per value head
+constexpr int COUNT_STRIDE = 64;
+__host__ __device__ __forceinline__ int64_t count_index(int c, int hv, int h)
+{
+    return ((int64_t)c * hv + h) * COUNT_STRIDE;
+}
+
+template <bool RAW_V, bool SIGNAL>
+__device__ __forceinline__ void chunk_body(ChunkShared<RAW_V> &L, const ScanArgs &p, const ChunkDims &d,
+                                           const VRawArgs &vr, const int bid, const OutSignal &sig)
+{
+    auto &sKP = L.sKP;
+    auto &sVH = L.sVH;
+    auto &sRaw = L.sRaw;
+    auto &sRawH = L.sRawH;
+    auto &sV = L.sV;
+    auto &sXP = L.sXP;
+    auto &sXR = L.sXR;
+    auto &sU = L.sU;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -647,8 +680,8 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     // the XCD-aware permutation
     constexpr int RB = 128 / CHUNK_ROWS;
     const int per_seq = d.hv * RB;
-    const int rank = (int)blockIdx.x / per_seq;
-    int w = (int)blockIdx.x - rank * per_seq;
+    const int rank = bid / per_seq;
+    int w = bid - rank * per_seq;
     if ((per_seq & 7) == 0) w = (w & 7) * (per_seq >> 3) + (w >> 3);
     const int rb = w % RB;
     const int h = w / RB;
@@ -793,9 +826,23 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t0 = 4 * kk + r, t1 = 16 + 4 * kk + r;
-                if (t0 < nv) ob[(uint32_t)t0 * vstride] = O0[r];
-                if (t1 < nv) ob[(uint32_t)t1 * vstride] = O1[r];
+                if constexpr (SIGNAL) {
+                    if (t0 < nv)
+                        __hip_atomic_store(ob + (uint32_t)t0 * vstride, O0[r], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    if (t1 < nv)
+                        __hip_atomic_store(ob + (uint32_t)t1 * vstride, O1[r], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    if (t0 < nv) ob[(uint32_t)t0 * vstride] = O0[r];
+                    if (t1 < nv) ob[(uint32_t)t1 * vstride] = O1[r];
+                }
             }
+        };
+        auto count_chunk = [&](int c) {
+            if (lane == 0)
+                __hip_atomic_fetch_add(sig.count + count_index(c, hv, h), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         };
         side_barrier();
         for (int c = 0; c < n_chunks; ++c) {
@@ -804,10 +851,30 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
             // reach the LDS first (~256 cycles)
             __builtin_amdgcn_s_sleep(4);
             if (c > 0) o_store(c - 1);
+            if constexpr (SIGNAL) {
+                if (c > 2) {
+                    // Chunk c - 3 is counted once its stores have completed.
+                    // The 16 stores of chunks c - 2 and c - 1 (full chunks:
+                    // each o_store issues 8 store instructions) followed
+                    // them, and vector-memory operations complete in order,
+                    // so at most 16 outstanding means those are done; the
+                    // stores were issued two steps ago, so the wait is
+                    // normally over already.  The empty asm statements keep
+                    // the compiler from moving memory operations across it.
+                    __asm__ volatile("" ::: "memory");
+                    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * 8));
+                    __asm__ volatile("" ::: "memory");
+                    count_chunk(c - 3);
+                }
+            }
             take_lam_m(c);
         }
         side_barrier();
         o_store(n_chunks - 1);
+        if constexpr (SIGNAL) {
+            wait_vmem_all();
+            for (int c = max(0, n_chunks - 3); c < n_chunks; ++c) count_chunk(c);
+        }
         return;
     }
 
@@ -1124,6 +1191,14 @@ __global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanAr
     for (int i = 0; i < 4; ++i) *reinterpret_cast<f4 *>(Srow + 16 * i) = S4[i] * (1.f / KQ_SCALE);
 }
 
+template <bool RAW_V>
+__global__ __launch_bounds__(chunk_threads(RAW_V)) void scan_chunk_kernel(ScanArgs p, ChunkDims d,
+                                                                         VRawArgs vr)
+{
+    __shared__ ChunkShared<RAW_V> L;
+    chunk_body<RAW_V, false>(L, p, d, vr, (int)blockIdx.x, OutSignal{nullptr});
+}
+
 static int64_t scan_slots(const gdn_shape &s)
 {
     return s.total_T / CT + (int64_t)s.n_seq + 1;
@@ -1291,6 +1366,12 @@ __global__ __launch_bounds__(256) void layer_prep_f16_kernel(LayerPrepArgs p, Pr
     if (c * CT >= T_n) return;
     const int nv = min(CT, T_n - c * CT);
     const int hk = d.hk, hv = d.hv, G = d.G, C = d.C;
+    if (p.sync) {
+        // (one sequence) the counters of chunk c's value heads of this group,
+        // and the status word, start at zero for the chunk kernel's post role
+        if (tid < G) p.sync[count_index(c, hv, j * G + tid)] = 0;
+        if (c == 0 && j == 0 && tid == 0) p.sync[count_index(d.n_chunk_max, hv, 0)] = 0;
+    }
     const _Float16 *qkv = static_cast<const _Float16 *>(p.qkv);
     const _Float16 *cw = static_cast<const _Float16 *>(p.conv_w);
     _Float16 *hist = static_cast<_Float16 *>(p.hist) + (int64_t)n * 3 * C;
@@ -1381,6 +1462,121 @@ __global__ __launch_bounds__(256) void layer_prep_f16_kernel(LayerPrepArgs p, Pr
     prep_body(sm, p.ws, d, j, chunk_slot(cu0, n, c), nv, g_next, b_next, load_gb);
 }
 
+// ---- post in the chunk kernel's launch ------------------------------------
+//
+// The chunk kernel leaves CUs idle (one block per (value head, 32 channels):
+// 192 blocks for 48 value heads on 256 CUs) and finishes o chunk by chunk,
+// while post needs all 128 channels of a (token, value head) row, which four
+// chunk blocks hold.  Here blocks past the chunk blocks run post: each wave
+// takes units (chunk c, value head h) in chunk order, waits until the eight
+// output waves of head h have counted chunk c (OutSignal), reads its 32 rows
+// of o with device-scope loads and writes y (the post kernel's arithmetic,
+// post_row).  The post blocks have the highest indices, so the chunk blocks,
+// which wait for nothing, are dispatched first: the launch completes whatever
+// the number of CUs.  A wait is bounded; past the bound the unit is computed
+// from whatever o holds (the results are then undefined) and bit 0 of the
+// status word is set.  Units of the value heads of XCD x run on XCD x (blocks
+// are dealt to the 8 XCDs in turn; the chunk blocks' permutation puts the
+// heads x hv / 8 .. there).
+struct PostRoleArgs {
+    const uint32_t *count;
+    uint32_t *status;
+    const _Float16 *z, *gamma;
+    void *y;
+    float eps;
+    int chunk_blocks, np;  // chunk blocks, post blocks
+    int T;                 // tokens of the one sequence
+    int xcd_affine;
+};
+// polls before a wait gives up: one sleeps ~0.8 us and waits for a load, so
+// 2^15 of them take roughly 30-100 ms
+constexpr int POST_WAIT_POLLS = 1 << 15;
+
+template <typename TO>
+__device__ __forceinline__ void post_role(const ScanArgs &p, const ChunkDims &d, const PostRoleArgs &pa)
+{
+    const int pb = (int)blockIdx.x - pa.chunk_blocks;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, l16 = lane & 15, rr = lane >> 4;
+    const int hv = d.hv;
+    const int n_chunks = (pa.T + CT - 1) / CT;
+    float gm[8];
+    load8_split(pa.gamma + l16 * 4, gm);
+    // units of this wave: XCD x = block % 8 takes heads hx x .. hx x + hx - 1
+    const int nw = pa.np * 8;  // post waves
+    int first, step, per_xcd_heads = 0;
+    if (pa.xcd_affine) {
+        per_xcd_heads = hv >> 3;
+        first = (pb >> 3) * 8 + wave;
+        step = nw >> 3;
+    } else {
+        first = pb * 8 + wave;
+        step = nw;
+    }
+    const int n_units = pa.xcd_affine ? n_chunks * per_xcd_heads : n_chunks * hv;
+    bool gave_up = false;
+    for (int u = first; u < n_units; u += step) {
+        int c, h;
+        if (pa.xcd_affine) {
+            c = u / per_xcd_heads;
+            h = (pb & 7) * per_xcd_heads + (u - c * per_xcd_heads);
+        } else {
+            c = u / hv;
+            h = u - c * hv;
+        }
+        const uint32_t *cnt = pa.count + count_index(c, hv, h);
+        for (int it = 0; !gave_up; ++it) {
+            const uint32_t v = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (v >= O_WRITERS) break;
+            if (it >= POST_WAIT_POLLS) {
+                gave_up = true;
+                if (lane == 0) __hip_atomic_fetch_or(pa.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __builtin_amdgcn_s_sleep(30);
+        }
+        const int nv = min(CT, pa.T - c * CT);
+        // rows (token 4 i + rr of the chunk), lane l16 takes channels 4 l16 ..
+        // + 3 and 64 + 4 l16 .. + 3; o through a buffer descriptor based at the
+        // unit's first row (offsets stay small), device-scope loads (sc1)
+        const int64_t row0 = (int64_t)c * CT * hv + h;
+        __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.o + row0 * 128), (short)0, 0x7fffffff, 0x00020000);
+        const uint32_t rstride = (uint32_t)hv * 128 * 4;  // bytes per token
+        f4 oa[8], ob[8];
+        float zz[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = 4 * i + rr;
+            const int tc = min(t, nv - 1);  // rows past the end: the last row, unused
+            const uint32_t off = (uint32_t)tc * rstride + (uint32_t)l16 * 16;
+            oa[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 16));
+            ob[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 256, 0, 16));
+            load8_split(pa.z + (row0 + (int64_t)tc * hv) * 128 + l16 * 4, zz[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = 4 * i + rr;
+            const float x[8] = {oa[i][0], oa[i][1], oa[i][2], oa[i][3], ob[i][0], ob[i][1], ob[i][2], ob[i][3]};
+            float out[8];
+            post_row(x, zz[i], gm, pa.eps, out);
+            if (t < nv) store8_split(static_cast<TO *>(pa.y) + (row0 + (int64_t)t * hv) * 128 + l16 * 4, out);
+        }
+    }
+}
+
+template <typename TO>
+__global__ __launch_bounds__(chunk_threads(true)) void layer_chunk_post_kernel(ScanArgs p, ChunkDims d,
+                                                                               VRawArgs vr, PostRoleArgs pa)
+{
+    __shared__ ChunkShared<true> L;
+    if ((int)blockIdx.x < pa.chunk_blocks) {
+        chunk_body<true, true>(L, p, d, vr, (int)blockIdx.x, OutSignal{const_cast<uint32_t *>(pa.count)});
+        return;
+    }
+    post_role<TO>(p, d, pa);
+}
+
 static PrepDims prep_dims(const gdn_shape &s)
 {
     PrepDims pd;
@@ -1395,8 +1591,7 @@ static PrepDims prep_dims(const gdn_shape &s)
     return pd;
 }
 
-static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_t st,
-                               const VRawArgs *vr = nullptr)
+static ChunkDims chunk_dims(const gdn_shape &s)
 {
     ChunkDims cd;
     cd.hk = s.hk;
@@ -1405,7 +1600,16 @@ static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_
     cd.n_seq = s.n_seq;
     cd.vh_base = scan_slots(s) * s.hk * SCAN_KH_FLOATS;
     cd.ms = -LO_SCALE;
-    const int64_t blocks = (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS);
+    return cd;
+}
+
+static int64_t chunk_blocks(const gdn_shape &s) { return (int64_t)s.n_seq * s.hv * (128 / CHUNK_ROWS); }
+
+static hipError_t launch_chunk(const gdn_shape &s, const ScanArgs &a, hipStream_t st,
+                               const VRawArgs *vr = nullptr)
+{
+    const ChunkDims cd = chunk_dims(s);
+    const int64_t blocks = chunk_blocks(s);
     if (vr)
         hipLaunchKernelGGL(scan_chunk_kernel<true>, dim3((unsigned)blocks), dim3(chunk_threads(true)), 0,
                            st, a, cd, *vr);
@@ -1425,20 +1629,85 @@ hipError_t launch_scan(const gdn_shape &s, const ScanArgs &a, hipStream_t st)
     return launch_chunk(s, a, st);
 }
 
-hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp, const ScanArgs &a,
-                             hipStream_t st)
+// Compute units of the current device (0 if the runtime cannot say), looked
+// up once per device.
+static int device_cus()
+{
+    constexpr int kMaxDevices = 256;
+    static std::atomic<int> cus[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Post blocks of the chunk launch for a shape (0: post runs as its own
+// launch): one sequence of fp16 rows, and at least 32 CUs left by the chunk
+// blocks (a multiple of 8, at most 64).  GDN_LAYER_POST_FUSED=0 in the
+// environment selects the separate launch.
+constexpr int POST_NP_MIN = 32, POST_NP_MAX = 64;
+static int post_blocks(const gdn_shape &s)
+{
+    if (s.io_dtype != GDN_F16 || s.n_seq != 1) return 0;
+    const char *e = getenv("GDN_LAYER_POST_FUSED");
+    if (e && e[0] == '0') return 0;
+    const int64_t free_cus = (int64_t)device_cus() - chunk_blocks(s);
+    const int np = (int)(std::min<int64_t>(free_cus, POST_NP_MAX) & ~(int64_t)7);
+    return np >= POST_NP_MIN ? np : 0;
+}
+
+// counters (one 256-byte line each) and the status word (a line of its own)
+size_t layer_sync_bytes(const gdn_shape &s)
+{
+    return ((size_t)(s.max_T + CT - 1) / CT * s.hv + 1) * COUNT_STRIDE * sizeof(uint32_t);
+}
+
+template <typename TO>
+static hipError_t launch_chunk_post(const gdn_shape &s, const ScanArgs &a, const VRawArgs &vr,
+                                    const PostRoleArgs &pa, hipStream_t st)
+{
+    hipLaunchKernelGGL(layer_chunk_post_kernel<TO>, dim3((unsigned)(pa.chunk_blocks + pa.np)),
+                       dim3(chunk_threads(true)), 0, st, a, chunk_dims(s), vr, pa);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp0, const ScanArgs &a,
+                             const PostArgs *post, bool *post_done, hipStream_t st)
 {
     const PrepDims pd = prep_dims(s);
     const dim3 grid((unsigned)(s.n_seq * (int64_t)pd.n_chunk_max), s.hk);
+    if (post_done) *post_done = false;
     if (s.io_dtype == GDN_F16) {
+        const int np = post && post_done && lp0.sync ? post_blocks(s) : 0;
+        LayerPrepArgs lp = lp0;
+        if (np == 0) lp.sync = nullptr;
         // v of the value heads is formed in the chunk kernel (VRawArgs)
         hipLaunchKernelGGL(layer_prep_f16_kernel, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const VRawArgs vr{lp.qkv, lp.conv_w, lp.hist, pd.C};
-        return launch_chunk(s, a, st, &vr);
+        if (np == 0) return launch_chunk(s, a, st, &vr);
+        PostRoleArgs pa;
+        pa.count = lp.sync;
+        pa.status = lp.sync + count_index(pd.n_chunk_max, s.hv, 0);
+        pa.z = static_cast<const _Float16 *>(post->z);
+        pa.gamma = static_cast<const _Float16 *>(post->gamma);
+        pa.y = post->y;
+        pa.eps = s.eps_rms;
+        pa.chunk_blocks = (int)chunk_blocks(s);
+        pa.np = np;
+        pa.T = (int)s.total_T;
+        pa.xcd_affine = s.hv % 8 == 0 && pa.chunk_blocks % 8 == 0;
+        e = s.out_dtype == GDN_F16 ? launch_chunk_post<_Float16>(s, a, vr, pa, st)
+                                   : launch_chunk_post<float>(s, a, vr, pa, st);
+        if (e == hipSuccess) *post_done = true;
+        return e;
     }
-    hipLaunchKernelGGL(layer_prep_kernel<float>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp, pd);
+    hipLaunchKernelGGL(layer_prep_kernel<float>, grid, dim3(CHUNK_PREP_THREADS), 0, st, lp0, pd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_chunk(s, a, st);

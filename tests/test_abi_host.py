@@ -50,8 +50,11 @@ def test_workspace_bytes():
     per_slot = 16 * 32768 + 48 * 6656   # per 32-token chunk: key-head and value-head parts
     scan = (T // 32 + 1 + 1) * per_slot
     assert B.gdn_scan_workspace_bytes(s) == scan
-    # fused fp16 path (3 value heads per key head): o and the scan scratch only
-    assert B.gdn_prefill_workspace_bytes(s) == r(T * 48 * 128 * 4) + r(scan)
+    # fused fp16 path (3 value heads per key head): o, the scan scratch, and a
+    # counter per (chunk, value head) and a status word, 256 bytes each, for
+    # post run in the chunk kernel's launch
+    sync = r((T // 32 * 48 + 1) * 256)
+    assert B.gdn_prefill_workspace_bytes(s) == r(T * 48 * 128 * 4) + r(scan) + sync
     # fused fp32 path: the fp32 v as well
     s32 = shape(total_T=2048, max_T=2048, io="f32")
     assert B.gdn_prefill_workspace_bytes(s32) == 2 * r(T * 48 * 128 * 4) + r(scan)

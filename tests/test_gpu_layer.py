@@ -253,3 +253,41 @@ def test_layer_group_sizes_match_oracle_and_stages(gpu, hk, hv, io):
     assert np.array_equal(np_(st.y).view(np.uint8), np_(ly.y).view(np.uint8))
     assert np.array_equal(np_(st.state).view(np.uint32), np_(ly.state).view(np.uint32))
     assert np.array_equal(np_(st.hist).view(np.uint8), np_(ly.hist).view(np.uint8))
+
+
+@pytest.mark.parametrize("hk,hv,T,out", [(16, 48, 2048, "f16"), (16, 48, 517, "f32"), (8, 16, 40, "f16"),
+                                         (2, 6, 1, "f16")])
+def test_post_in_chunk_launch_equals_separate_post(gpu, hk, hv, T, out, monkeypatch):
+    # post run by the chunk kernel's launch (its idle CUs; each (chunk, value
+    # head) once its eight output waves have counted it) gives the separate
+    # post kernel's y bit for bit, on workspaces first filled with 0xFF bytes
+    # and with random bytes; the status word shows that no wait gave up.
+    # (16 and 8 key heads: value heads of XCD x on XCD x; 6 value heads: in
+    # plain chunk order)
+    w = synth.Workload("post_fused", hk=hk, hv=hv, seqlens=(T,), seed=(43,), io="f16", out=out,
+                       s0_std=0.05, hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", "post in the chunk launch vs separate", f"hk={hk} hv={hv} T={T} out={out}")
+    monkeypatch.setenv("GDN_LAYER_POST_FUSED", "0")
+    sep = _run_layer(w, inp)
+    monkeypatch.delenv("GDN_LAYER_POST_FUSED")
+    nbytes = B.gdn_prefill_workspace_bytes(sep.shape)
+    n_count = (T + 31) // 32 * hv
+    sync_at = nbytes - (n_count + 1) * 256   # the last region: a 256-byte line per counter
+    status_at = sync_at + n_count * 256
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for fill in ("ff", "random"):
+        if fill == "ff":
+            src = torch.full((nbytes,), 255, dtype=torch.uint8)
+        else:
+            src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
+        buf = LayerBuffers.create(w, inp)
+        ws = buf.workspace()
+        ws.copy_(src.cuda())
+        buf.run_layer(ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(buf.y).view(np.uint8), np_(sep.y).view(np.uint8)), fill
+        assert np.array_equal(np_(buf.state).view(np.uint32), np_(sep.state).view(np.uint32)), fill
+        assert np.array_equal(np_(buf.hist).view(np.uint16), np_(sep.hist).view(np.uint16)), fill
+        status = ws[status_at:status_at + 4].cpu().numpy().view(np.uint32)[0]
+        assert status == 0, f"a wait for o gave up ({fill})"
