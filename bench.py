@@ -252,7 +252,26 @@ def main():
             step()
         e1.record(stream)
         torch.cuda.synchronize()
-        return dict(ms_per_step=e0.elapsed_time(e1) / steps)
+        ms = e0.elapsed_time(e1) / steps
+
+        # the same 36-layer step captured once in a HIP graph and replayed (no
+        # host launches per layer); the calls go to the current stream, which
+        # is the capture stream while the graph is captured
+        def step_cur():
+            for l, d in enumerate(layers):
+                B.gdn_prefill_layer(shape, cu, d["qkv"], d["conv_w"], d["a"], d["b"], d["A_log"],
+                                    d["dt_bias"], d["z"], d["gamma"], d["hist"], d["S0"], ys[l], ws)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_cur()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return dict(ms_per_step=ms, ms_per_step_graph=e0.elapsed_time(e1) / steps)
 
     def run(out, steps, warmup):
         # the staged path (gdn_pre, gdn_scan, gdn_post per layer): the whole pass
@@ -513,8 +532,12 @@ def main():
                    "head_dim": 128, "io": "fp16", "state": "fp32", "out": "fp16",
                    "parallelism": "single-gpu"},
         "roofline": roof,
+        "graph_replay": {"value": round(T / (l16.get("ms_per_step_graph", float("nan")) / 1e3), 1),
+                         "unit": "tokens/s",
+                         "ms_per_step": round(l16.get("ms_per_step_graph", float("nan")), 4)},
         "fp32_out": {"value": round(T / (l32["ms_per_step"] / 1e3), 1), "unit": "tokens/s",
-                     "ms_per_step": round(l32["ms_per_step"], 4)},
+                     "ms_per_step": round(l32["ms_per_step"], 4),
+                     "graph_replay_ms_per_step": round(l32.get("ms_per_step_graph", float("nan")), 4)},
         "staged_fp16_out": {"value": round(T / (r16["ms_per_step"] / 1e3), 1),
                             "ms_per_step": round(r16["ms_per_step"], 4), **stage_report(r16, 2)},
         "staged_fp32_out": {"value": round(T / (r32["ms_per_step"] / 1e3), 1),
