@@ -1487,6 +1487,7 @@ struct PostRoleArgs {
     int chunk_blocks, np;  // chunk blocks, post blocks
     int T;                 // tokens of the one sequence
     int xcd_affine;
+    int max_polls;         // polls before a wait gives up
 };
 // polls before a wait gives up: one sleeps ~0.8 us and waits for a load, so
 // 2^15 of them take roughly 30-100 ms
@@ -1529,7 +1530,7 @@ __device__ __forceinline__ void post_role(const ScanArgs &p, const ChunkDims &d,
             const uint32_t v = __builtin_amdgcn_readfirstlane(
                 __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
             if (v >= O_WRITERS) break;
-            if (it >= POST_WAIT_POLLS) {
+            if (it >= pa.max_polls) {
                 gave_up = true;
                 if (lane == 0) __hip_atomic_fetch_or(pa.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -1702,6 +1703,10 @@ hipError_t launch_layer_scan(const gdn_shape &s, const LayerPrepArgs &lp0, const
         pa.np = np;
         pa.T = (int)s.total_T;
         pa.xcd_affine = s.hv % 8 == 0 && pa.chunk_blocks % 8 == 0;
+        // (GDN_POST_WAIT_POLLS in the environment lowers the bound, so that
+        // a test can take the give-up path without anything going wrong)
+        pa.max_polls = POST_WAIT_POLLS;
+        if (const char *e = getenv("GDN_POST_WAIT_POLLS")) pa.max_polls = std::max(0, std::min(atoi(e), POST_WAIT_POLLS));
         e = s.out_dtype == GDN_F16 ? launch_chunk_post<_Float16>(s, a, vr, pa, st)
                                    : launch_chunk_post<float>(s, a, vr, pa, st);
         if (e == hipSuccess) *post_done = true;

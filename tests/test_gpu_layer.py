@@ -291,3 +291,34 @@ def test_post_in_chunk_launch_equals_separate_post(gpu, hk, hv, T, out, monkeypa
         assert np.array_equal(np_(buf.hist).view(np.uint16), np_(sep.hist).view(np.uint16)), fill
         status = ws[status_at:status_at + 4].cpu().numpy().view(np.uint32)[0]
         assert status == 0, f"a wait for o gave up ({fill})"
+
+
+def test_post_in_chunk_launch_wait_bound(gpu, monkeypatch):
+    # the post waves' wait for o is bounded: with the bound forced to zero
+    # polls from the host, they give up at once, the call still completes and
+    # the status word says so; the next call with the normal bound is exact
+    w = synth.Workload("post_bound", hk=16, hv=48, seqlens=(300,), seed=(44,), s0_std=0.05,
+                       hist_std=1.0)
+    inp = synth.layer_inputs(w)
+    banner("gdn_prefill_layer", "post wait bound forced to 0")
+    monkeypatch.setenv("GDN_LAYER_POST_FUSED", "0")
+    sep = _run_layer(w, inp)
+    monkeypatch.delenv("GDN_LAYER_POST_FUSED")
+    nbytes = B.gdn_prefill_workspace_bytes(sep.shape)
+    n_count = (300 + 31) // 32 * 48
+    status_at = nbytes - 256
+    assert status_at == nbytes - (n_count + 1) * 256 + n_count * 256
+    buf = LayerBuffers.create(w, inp)
+    ws = buf.workspace()
+    monkeypatch.setenv("GDN_POST_WAIT_POLLS", "0")
+    buf.run_layer(ws)
+    torch.cuda.synchronize()
+    assert ws[status_at:status_at + 4].cpu().numpy().view(np.uint32)[0] & 1 == 1
+    # the state and history do not depend on post
+    assert np.array_equal(np_(buf.state).view(np.uint32), np_(sep.state).view(np.uint32))
+    monkeypatch.delenv("GDN_POST_WAIT_POLLS")
+    again = LayerBuffers.create(w, inp)
+    again.run_layer(ws)
+    torch.cuda.synchronize()
+    assert ws[status_at:status_at + 4].cpu().numpy().view(np.uint32)[0] == 0
+    assert np.array_equal(np_(again.y).view(np.uint16), np_(sep.y).view(np.uint16))
