@@ -205,6 +205,20 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape);
  * (>= gdn_prefill_workspace_bytes(shape) bytes, device memory, 256-byte
  * aligned, contents undefined afterwards, not shared by calls in flight at the
  * same time).  hist and state are read and overwritten in place.
+ *
+ * With fp16 io, one sequence, hv/hk <= 8 and at least 32 CUs left free by
+ * the chunk kernel's blocks (one per sequence, value head and 32 value
+ * channels), post runs inside that kernel's launch on those CUs, each (chunk,
+ * value head) once the chunk's o values of that head are stored (the result
+ * is bit for bit that of the separate post).  Each of those waits is bounded (about 30-100 ms;
+ * the environment variable GDN_POST_WAIT_POLLS, read at each call, can lower
+ * the bound, GDN_LAYER_POST_FUSED=0 selects the separate post launch).  A wait
+ * that runs out leaves y undefined for that unit (state and hist are not
+ * affected) and sets bit 0 of the 32-bit word at byte offset
+ * gdn_prefill_workspace_bytes(shape) - 256 of the workspace, which is 0
+ * after a call in which no wait ran out; read it once the call has completed.
+ * Only a device that cannot run the chunk blocks to completion (every chunk
+ * block is dispatched before any post block) lets a wait run out.
  */
 int gdn_prefill_layer(const gdn_shape *shape, const int32_t *cu_seqlens,
                       const void *qkv, const void *conv_w, const void *a,
