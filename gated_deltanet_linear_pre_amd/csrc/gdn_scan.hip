@@ -1525,6 +1525,15 @@ __device__ __forceinline__ void post_role(const ScanArgs &p, const ChunkDims &d,
             c = u / hv;
             h = u - c * hv;
         }
+        // z does not depend on the chunk step: requested before the wait
+        const int nv = min(CT, pa.T - c * CT);
+        const int64_t row0 = (int64_t)c * CT * hv + h;
+        float zz[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tc = min(4 * i + rr, nv - 1);
+            load8_split(pa.z + (row0 + (int64_t)tc * hv) * 128 + l16 * 4, zz[i]);
+        }
         const uint32_t *cnt = pa.count + count_index(c, hv, h);
         for (int it = 0; !gave_up; ++it) {
             const uint32_t v = __builtin_amdgcn_readfirstlane(
@@ -1534,18 +1543,17 @@ __device__ __forceinline__ void post_role(const ScanArgs &p, const ChunkDims &d,
                 gave_up = true;
                 if (lane == 0) __hip_atomic_fetch_or(pa.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            __builtin_amdgcn_s_sleep(30);
+            // the last chunks: the launch ends with them, poll often
+            if (c + 4 >= n_chunks) __builtin_amdgcn_s_sleep(2);
+            else __builtin_amdgcn_s_sleep(30);
         }
-        const int nv = min(CT, pa.T - c * CT);
         // rows (token 4 i + rr of the chunk), lane l16 takes channels 4 l16 ..
         // + 3 and 64 + 4 l16 .. + 3; o through a buffer descriptor based at the
         // unit's first row (offsets stay small), device-scope loads (sc1)
-        const int64_t row0 = (int64_t)c * CT * hv + h;
         __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(p.o + row0 * 128), (short)0, 0x7fffffff, 0x00020000);
         const uint32_t rstride = (uint32_t)hv * 128 * 4;  // bytes per token
         f4 oa[8], ob[8];
-        float zz[8][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = 4 * i + rr;
@@ -1553,7 +1561,6 @@ __device__ __forceinline__ void post_role(const ScanArgs &p, const ChunkDims &d,
             const uint32_t off = (uint32_t)tc * rstride + (uint32_t)l16 * 16;
             oa[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 16));
             ob[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ro, off + 256, 0, 16));
-            load8_split(pa.z + (row0 + (int64_t)tc * hv) * 128 + l16 * 4, zz[i]);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
