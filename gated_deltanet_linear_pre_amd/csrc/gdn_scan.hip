@@ -362,36 +362,62 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
         // beta of tokens 4 kk .. 4 kk + 3 and 16 + 4 kk .. 16 + 4 kk + 3
         const f4 b4a = *reinterpret_cast<const f4 *>(&sm.sGB[wave][1][4 * kk]);
         const f4 b4b = *reinterpret_cast<const f4 *>(&sm.sGB[wave][1][16 + 4 * kk]);
-        // Every decay is the exp of a direct sum of the log decays it spans,
-        // summed in token order: lane s < 32 walks its column, D[t][s] =
-        // exp(g_{s+1} + ... + g_t) for t > s (0 above the diagonal, and 1 on
-        // it, written after the walk), into sT (free until T is formed);
-        // lanes 32.. take the prefix sums from the chunk start, into sT's
-        // padding columns: Lam_t = exp(g_0 + ... + g_t) in column 32, the sum
-        // itself in column 33.  The walk has no comparison: whether token t
-        // counts for column s is the sign of s - t.
+        // Every decay is the exp of a sum of the log decays it spans, each
+        // sum taken in token order within one 16-token half of the chunk.
+        // The walk covers the two diagonal blocks at once in 16 steps: lane
+        // s < 16 walks column s over tokens 0..15 and lane 16 + s' column
+        // 16 + s' over tokens 16..31, D[t][s] = exp(g_{s+1} + ... + g_t) for
+        // t > s (0 above the diagonal, 1 on it, written after the walk), into
+        // sT (free until T is formed).  Lanes 32 and 33 take the sums from
+        // the chunk start over tokens 0..15 (Lam_t = exp of it in column 32,
+        // the sum in column 33), lanes 34 and 35 those from token 16 over
+        // tokens 16..31 (exp of it, D[t][15], in column 15, the sum in column
+        // 34).  The walk has no comparison: whether token t counts for a lane
+        // is the sign of its start column minus t.  Then the block below the
+        // diagonal ones is D[t][s] = D[t][15] D[15][s] (t >= 16 > s; both
+        // factors <= 1), and Lam_t for t >= 16 is exp(S_15 + sum_{16..t}).
         {
-            const int s = lane_o & 31;
-            const bool pref = lane_o >= 32;
-            const int colw = pref ? (lane_o >= 48 ? 33 : 32) : s;
-            const uint32_t allm = pref ? 0xffffffffu : 0u;
-            const bool wsum = lane_o >= 48;
+            const bool second = (lane_o >= 16 && lane_o < 32) || lane_o >= 34;
+            const int s0 = lane_o < 32 ? (lane_o & 31) : (lane_o < 34 ? -1 : 15);
+            // column each lane writes: its own, 32/33, 15/34; lanes past 35
+            // (and their unused results) go to padding column 35
+            const int colw = lane_o < 32 ? lane_o : lane_o == 32 ? 32 : lane_o == 33 ? 33
+                           : lane_o == 34 ? 15 : lane_o == 35 ? 34 : 35;
+            const bool wsum = lane_o == 33 || lane_o == 35;
+            const int tb = second ? CT / 2 : 0;
             float acc = 0.f;
 #pragma unroll
-            for (int t = 0; t < CT; ++t) {
-                const uint32_t m = (uint32_t)((s - t) >> 31) | allm;  // all ones if t counts
-                acc += __uint_as_float(__float_as_uint(gv[t]) & m);
+            for (int i = 0; i < CT / 2; ++i) {
+                const int t = tb + i;
+                const float gi = second ? gv[CT / 2 + i] : gv[i];
+                const uint32_t m = (uint32_t)((s0 - t) >> 31);  // all ones if t counts
+                acc += __uint_as_float(__float_as_uint(gi) & m);
                 const float e = exp_fast(acc);
                 sT[t][colw] = __uint_as_float(__float_as_uint(wsum ? acc : e) & m);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (!pref) sT[s][s] = 1.f;
+            {
+                // rows 16 + (lane % 16), columns 4 (lane / 16) .. + 3 (but 15)
+                const int t = CT / 2 + l16, sb = 4 * kk;
+                const float dt = sT[t][15];
+                const f4 d15 = *reinterpret_cast<const f4 *>(&sT[15][sb]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (sb + k < 15) sT[t][sb + k] = dt * d15[k];
+                if (lane_o < CT) sT[lane_o][lane_o] = 1.f;
+                if (lane_o >= CT / 2 && lane_o < CT) {
+                    const float st = sT[15][33] + sT[lane_o][34];
+                    sT[lane_o][33] = st;
+                    sT[lane_o][32] = exp_fast(st);
+                }
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (!pref) {
+            if (lane_o < CT) {
+                const int s = lane_o;
                 // Lam_t and D[last][t] weight this chunk's terms only
                 vs[VH_LAM + s] = s < nv_o ? sT[s][32] * (1.f / (KQ_SCALE * KQ_SCALE)) : 0.f;
                 vs[VH_BETA + s] = b_own;
