@@ -19,8 +19,10 @@
 //   S' = Lam_last S0 + sum_s D[last][s] u_s k_s^T
 // with P = K S0^T, R = Q S0^T (tokens x value channels).  This is exact
 // algebra of the recurrence (unroll S_t = Lam_t S0 + sum_{s<=t} D[t][s] u_s k_s^T).
-// Every decay is formed as exp of a sum of at most 32 log decays, never as a
-// ratio of two cumulative products, so nothing overflows or cancels.
+// Every decay is formed as exp of a sum of at most 16 log decays (one half of
+// the chunk), or as the product of two such decays (both <= 1) when it spans
+// both halves; never as a ratio of two cumulative products, so nothing
+// overflows or cancels.
 //
 // Precision.  Every product of the chunk step runs on fp16 MFMA with fp32
 // accumulation, each fp32 operand x split into hi = fp16(x) and
