@@ -731,6 +731,9 @@ __device__ __forceinline__ void chunk_body(ChunkShared<RAW_V> &L, const ScanArgs
         typedef void __attribute__((address_space(3))) *lptr_t;
         constexpr int K_PIECES = KH_HALF_FLOATS * 4 / 1024;                        // 16
         constexpr int VH_PIECES = SCAN_SLOT_FLOATS * 4 / 1024;                      // 6 (+ 512 B)
+        // load instructions per issue_vh and issue_raw
+        constexpr int VH_COPIES = VH_PIECES + 2 + (RAW_V ? 0 : 4);
+        constexpr int RAW_COPIES = RAW_V ? 2 : 0;
         auto copy16 = [](const void *src, void *lds_piece) {
             __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_piece, 16, 0, 0);
         };
@@ -791,13 +794,21 @@ __device__ __forceinline__ void chunk_body(ChunkShared<RAW_V> &L, const ScanArgs
         // c + 2's K (read during step c + 1), chunk c + 1's value-head slot
         // and fp32 v, and with RAW_V chunk c + 2's raw rows (the v wave turns
         // them into v between the barriers of steps c + 1 and c + 2).
+        // what is read before the barrier of step 0 first (chunk 0's K for
+        // the compute waves' first products, its raw rows for the v wave),
+        // then what is read after it
         issue_k(0);
-        if (n_chunks > 1) issue_k(1);
-        issue_vh(0);
         issue_raw(0);
-        if (n_chunks > 1) issue_raw(1);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        issue_vh(0);
+        if (n_chunks > 1) {
+            issue_k(1);
+            issue_raw(1);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(K_PIECES + VH_COPIES + RAW_COPIES));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(VH_COPIES));
+        }
         side_barrier();
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         for (int c = 0; c < n_chunks; ++c) {
             side_barrier();
             if (c + 2 < n_chunks) issue_k(c + 2);
@@ -934,8 +945,6 @@ __device__ __forceinline__ void chunk_body(ChunkShared<RAW_V> &L, const ScanArgs
             // the old history rows of the block's channels (lanes 0..11)
             Raw8<_Float16> hrow;
             if (lane < 12) hrow.load(hist + (int64_t)(lane >> 2) * C + cv + g8);
-            wait_vmem_all();
-            if (lane < 12) *reinterpret_cast<h8 *>(&sRawH[lane >> 2][g8]) = hrow.v;
             // taps of token t: raw rows t - 3 .. t, reaching into the previous
             // chunk's rows (or the history, for chunk 0)
             auto conv_chunk = [&](int c) {
@@ -962,7 +971,11 @@ __device__ __forceinline__ void chunk_body(ChunkShared<RAW_V> &L, const ScanArgs
                     *reinterpret_cast<f4 *>(&sV[vb][t][g8 + 4]) = s1;
                 }
             };
+            // the weights and history rows arrive while the other waves
+            // wait for chunk 0's operands (sRawH is this wave's own)
             side_barrier();
+            wait_vmem_all();
+            if (lane < 12) *reinterpret_cast<h8 *>(&sRawH[lane >> 2][g8]) = hrow.v;
             conv_chunk(0);
             for (int c = 0; c < n_chunks; ++c) {
                 side_barrier();
