@@ -235,6 +235,17 @@ __device__ __forceinline__ int64_t chunk_slot(int cu0, int n, int c)
     return (int64_t)(cu0 >> 5) + c + n;
 }
 
+// A 16-byte store of a prep slot that writes through the L2 (the buffer
+// store's sc1 cache-policy bit): only the next launch reads the slots, and a
+// launch that leaves fewer dirty L2 lines behind hands over to the next one
+// sooner (36-layer prefill +0.6%).  base is the same for the whole wave.
+__device__ __forceinline__ void store_slot(_Float16 *base, int off_halves, h8 v)
+{
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off_halves * 2, 0, 16);
+}
+
 struct PrepDims {
     int hk, hv, G, n_chunk_max;
     float m1;         // -1 (see lo_pair)
@@ -299,10 +310,10 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             }
             split8<false>(ka, kb, khi[tau], klo[tau], d.m1);
             split8<false>(qa, qb, qhi[tau], qlo[tau], d.m1);
-            *reinterpret_cast<h8 *>(kh + KH_KP + kp_off(tau, s, 0) + kpos(lane) * 8) = khi[tau];
-            *reinterpret_cast<h8 *>(kh + KH_KP + kp_off(tau, s, 1) + kpos(lane) * 8) = klo[tau];
-            *reinterpret_cast<h8 *>(kh + KH_QP + kp_off(tau, s, 0) + lane * 8) = qhi[tau];
-            *reinterpret_cast<h8 *>(kh + KH_QP + kp_off(tau, s, 1) + lane * 8) = qlo[tau];
+            store_slot(kh, KH_KP + kp_off(tau, s, 0) + kpos(lane) * 8, khi[tau]);
+            store_slot(kh, KH_KP + kp_off(tau, s, 1) + kpos(lane) * 8, klo[tau]);
+            store_slot(kh, KH_QP + kp_off(tau, s, 0) + lane * 8, qhi[tau]);
+            store_slot(kh, KH_QP + kp_off(tau, s, 1) + lane * 8, qlo[tau]);
         }
         // as A and as B operand, lane (t, kk) holds the same row of keys, so
         // the product is X Y^T over this key step (x 256)
@@ -455,11 +466,11 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             h4 hi, lo;
             split4<false>(m00, hi, lo, d.m1);
             _Float16 *mp = reinterpret_cast<_Float16 *>(vs + VH_MP);
-            *reinterpret_cast<h8 *>(mp + lane * 8) = cat(hi, lo);
+            store_slot(mp, lane * 8, cat(hi, lo));
             h8 h1, l1;
             split8<false>(m1a, m1b, h1, l1, d.m1);
-            *reinterpret_cast<h8 *>(mp + 512 + lane * 8) = h1;
-            *reinterpret_cast<h8 *>(mp + 1024 + lane * 8) = l1;
+            store_slot(mp, 512 + lane * 8, h1);
+            store_slot(mp, 1024 + lane * 8, l1);
         }
         // the wave's A writes must land before its lanes read them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -525,11 +536,11 @@ __device__ __forceinline__ void prep_body(PrepShared &sm, float *ws, const PrepD
             h4 hi, lo;
             split4<false>(t00, hi, lo, d.m1);
             _Float16 *tp = reinterpret_cast<_Float16 *>(vs + VH_TP);
-            *reinterpret_cast<h8 *>(tp + lane * 8) = cat(hi, lo);
+            store_slot(tp, lane * 8, cat(hi, lo));
             h8 h1, l1;
             split8<false>(t1a, t1b, h1, l1, d.m1);
-            *reinterpret_cast<h8 *>(tp + 512 + lane * 8) = h1;
-            *reinterpret_cast<h8 *>(tp + 1024 + lane * 8) = l1;
+            store_slot(tp, 512 + lane * 8, h1);
+            store_slot(tp, 1024 + lane * 8, l1);
         }
         // every lane is done with A and T before the next head overwrites them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
